@@ -1,0 +1,229 @@
+/*
+ * moe.h - C ABI of libmoe: the inference forward of a DeepSeek-V3 / Kimi style
+ * routed mixture-of-experts block on one AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these web pages, which quote the models' source:
+ *   [K2-AFF]  "Kimi K2 - Affinities" (OpenModelAtlas), gate-forward excerpt
+ *             (MoEGate.forward) and gate-init excerpt (MoEGate.__init__)
+ *   [V32-AFF] "DeepSeek-V3.2-Exp - Affinities", gate-forward and gate-init
+ *             excerpts (Gate.forward, Gate.__init__)
+ *   [K3-ADD]  "Kimi K3 - Add shared output" (prefill), moe-forward excerpt
+ *             (KimiSparseMoeBlock.forward and moe_infer)
+ *   [K3-GATE] "Kimi K3 - Gate features" (decode), expert excerpt
+ *             (KimiBlockSparseMLP) and situ excerpt (SituAndMul)
+ *
+ * Conventions for every call below.
+ *  - Tensor arguments are DEVICE pointers to memory the caller owns (e.g.
+ *    allocated by PyTorch); libmoe allocates no memory and frees none.
+ *    Scratch space comes from the caller's `workspace` (device memory of at
+ *    least moe_workspace_size(...) bytes, 256-byte aligned); its contents on
+ *    entry are ignored and on return are unspecified.
+ *  - All tensors are dense and row-major, with the shapes given per call.
+ *    Weight matrices use the nn.Linear layout [out_features, in_features].
+ *    Element type "dtype" is cfg->dtype (fp32, or bf16 as 16-bit patterns);
+ *    the router weight, the correction bias, routing weights and the latent
+ *    norm weight are always fp32; indices are int32.
+ *  - Every tensor pointer must be non-NULL (unless marked optional) and
+ *    16-byte aligned; every width (d, d_ff, d_latent, d_ff_shared) must be a
+ *    positive multiple of 8.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without waiting for it.  Outputs are valid once the
+ *    stream reaches that point.  Calls never synchronise with the host.
+ *  - Arguments are validated on the host before anything is enqueued.  On an
+ *    error nothing is enqueued, outputs are untouched, the status says why and
+ *    moe_last_error() gives a message.  No C++ exception crosses this ABI.
+ *  - Calls on one stream are ordered; concurrent calls on different streams
+ *    must not share outputs or a workspace.
+ *  - Results are deterministic: the same inputs give the same bits.
+ */
+#ifndef LIBMOE_MOE_H
+#define LIBMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* bad shape, pointer, alignment or config value */
+  MOE_ERR_UNSUPPORTED = 2, /* a mode the pages allow but libmoe does not run */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  MOE_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} moe_status;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
+
+/* [K3-GATE]: experts use SiLU (act_fn(w1 x) * w3 x) or SiTU. */
+typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SITU = 1 } moe_act;
+
+/* [V32-AFF] offers softmax scoring; libmoe runs sigmoid only ([K2-AFF]). */
+typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score_func;
+
+/* [K2-AFF] raises for any top-k method other than noaux_tc. */
+typedef enum { MOE_TOPK_NOAUX_TC = 0 } moe_topk_method;
+
+/* Which call a workspace is sized for (moe_workspace_size). */
+typedef enum {
+  MOE_CALL_ROUTE = 0,
+  MOE_CALL_PERMUTE = 1,
+  MOE_CALL_GATE_UP = 2,
+  MOE_CALL_DOWN = 3,
+  MOE_CALL_COMBINE = 4,
+  MOE_CALL_BLOCK = 5
+} moe_call;
+
+/* Block configuration; field names follow the pages' config fields. */
+typedef struct {
+  int64_t d;               /* hidden_size: router input width and block width */
+  int64_t n_experts;       /* E = n_routed_experts, 2 <= E <= 1024 */
+  int32_t n_group;         /* G = n_group; E % G == 0 and E / G >= 2 */
+  int32_t topk_group;      /* TG = topk_group, 1 <= TG <= G */
+  int32_t top_k;           /* k = num_experts_per_tok, 1 <= k <= min(16, TG * E / G) */
+  int32_t norm_topk_prob;  /* renormalise the k weights (applied only when k > 1) */
+  float route_scale;       /* routed_scaling_factor */
+  int32_t score_func;      /* moe_score_func: SIGMOID (SOFTMAX -> MOE_ERR_UNSUPPORTED) */
+  int32_t topk_method;     /* moe_topk_method: NOAUX_TC */
+  int32_t training;        /* must be 0: inference only (training -> UNSUPPORTED) */
+  int64_t d_ff;            /* moe_intermediate_size of a routed expert */
+  int32_t act;             /* moe_act, for routed and shared experts */
+  float situ_beta;         /* activation_situ_beta; 0 means 1.0 */
+  float situ_linear_beta;  /* activation_situ_linear_beta; <= 0 means none */
+  int64_t d_latent;        /* L: width of the latent experts; 0 = no latent MoE */
+  int32_t latent_norm;     /* latent_moe_use_norm */
+  float norm_eps;          /* epsilon of the latent RMS norm */
+  int64_t d_ff_shared;     /* intermediate width of the shared expert; 0 = none */
+  int32_t dtype;           /* moe_dtype of hidden, weights (but router/bias/gamma), outputs */
+} moe_config;
+
+/* Weights of one block.  d_in = d_latent if d_latent > 0, else d. */
+typedef struct {
+  const float* w_router;  /* [E, d] fp32 router weight ([K2-AFF] gate-init) */
+  const float* bias;      /* [E] fp32 e_score_correction_bias, choice only */
+  const void* w1;         /* [E, d_ff, d_in] dtype, gate projections */
+  const void* w3;         /* [E, d_ff, d_in] dtype, up projections */
+  const void* w2;         /* [E, d_in, d_ff] dtype, down projections */
+  const void* w_down;     /* [L, d] dtype, latent down projection (latent only) */
+  const float* gamma;     /* [L] fp32, latent RMS-norm weight (latent_norm only) */
+  const void* w_up;       /* [d, L] dtype, latent up projection (latent only) */
+  const void* sh_w1;      /* [d_ff_shared, d] dtype, shared gate (shared only) */
+  const void* sh_w3;      /* [d_ff_shared, d] dtype, shared up */
+  const void* sh_w2;      /* [d, d_ff_shared] dtype, shared down */
+} moe_weights;
+
+/* Host-only helpers (no device work). */
+const char* moe_status_str(moe_status s);
+/* Message for the last error returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+/* Checks a configuration alone: the limits listed in moe_config. */
+moe_status moe_validate_config(const moe_config* cfg);
+/* Workspace bytes `call` needs for N tokens (0 for MOE_CALL_COMBINE). */
+moe_status moe_workspace_size(const moe_config* cfg, int64_t N, int32_t call, size_t* bytes);
+
+/*
+ * moe_route - the router ([K2-AFF] gate-forward; [V32-AFF] gate-forward).
+ *   logits = hidden . w_router^T in fp32 (hidden widened exactly), no bias;
+ *   score = sigmoid(logits); choice = score + bias (selection only);
+ *   group g = experts [g*E/G, (g+1)*E/G); group score = sum of its two largest
+ *   choice values; the TG best groups are kept and the others dropped (their
+ *   experts can never be chosen); the k largest choice values among the kept
+ *   experts are chosen (ties to the lower index); weight = score of the chosen
+ *   expert, divided by (sum of the k scores + 1e-20) when norm_topk_prob and
+ *   k > 1, times route_scale.
+ * hidden [N, d] dtype; w_router [E, d] fp32; bias [E] fp32.
+ * Out: topk_idx [N, k] int32, each row's experts in ascending id;
+ *      topk_weight [N, k] fp32, in the same slot order.
+ * N = 0 is a valid no-op.
+ */
+moe_status moe_route(const moe_config* cfg, int64_t N, const void* hidden, const float* w_router,
+                     const float* bias, int32_t* topk_idx, float* topk_weight, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * moe_permute - dispatch by expert ([K3-ADD] moe_infer: the per-expert token
+ * counts, the argsort of the flattened choices, the gather of token rows).
+ *   tokens_per_expert[e] = number of slots (n, j) with topk_idx[n][j] == e;
+ *   expert_offsets = exclusive prefix sum (expert_offsets[E] = N*k);
+ *   perm[p] = flat slot n*k + j at sorted position p: slots grouped by expert
+ *   and, inside an expert, in increasing slot order (a stable sort);
+ *   inv_perm[n*k + j] = p;  x_sorted[p] = x_in[perm[p] / k].
+ * topk_idx [N, k] int32: each row must hold k distinct experts in [0, E) (as
+ *   moe_route writes them); other values give unspecified outputs but no
+ *   access outside the arguments.
+ * x_in [N, d_in] dtype: the experts' input (the latent input when d_latent > 0).
+ * Out: tokens_per_expert [E], expert_offsets [E + 1], perm [N*k], inv_perm
+ *   [N*k] int32; x_sorted [N*k, d_in] dtype (optional: NULL skips the gather).
+ */
+moe_status moe_permute(const moe_config* cfg, int64_t N, const int32_t* topk_idx,
+                       const void* x_in, int32_t* tokens_per_expert, int32_t* expert_offsets,
+                       int32_t* perm, int32_t* inv_perm, void* x_sorted, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * moe_expert_gate_up - first half of every routed expert ([K3-GATE] expert
+ * and situ excerpts), on the expert-sorted rows.  For each expert e and row p
+ * in [expert_offsets[e], expert_offsets[e+1]):
+ *   g = w1[e] . x_sorted[p], u = w3[e] . x_sorted[p] (fp32 accumulation),
+ *   SiLU: h = silu(g) * u;
+ *   SiTU: h = beta*tanh(g/beta)*sigmoid(g) * (lb*tanh(u/lb) if lb > 0 else u),
+ *   evaluated in fp32 and rounded once to dtype.
+ * x_sorted [N*k, d_in] dtype; expert_offsets [E + 1] int32 as moe_permute
+ * writes it (non-decreasing, from 0 to N*k); w1, w3 [E, d_ff, d_in] dtype.
+ * Out: h_sorted [N*k, d_ff] dtype.
+ */
+moe_status moe_expert_gate_up(const moe_config* cfg, int64_t N, const void* x_sorted,
+                              const int32_t* expert_offsets, const void* w1, const void* w3,
+                              void* h_sorted, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * moe_expert_down - second half of every routed expert ([K3-GATE] expert:
+ * w2 applied to the activation).  out_sorted[p] = w2[e] . h_sorted[p] for the
+ * rows p of expert e, fp32 accumulation, rounded once to dtype.
+ * h_sorted [N*k, d_ff] dtype; expert_offsets as above; w2 [E, d_in, d_ff].
+ * Out: out_sorted [N*k, d_in] dtype.
+ */
+moe_status moe_expert_down(const moe_config* cfg, int64_t N, const void* h_sorted,
+                           const int32_t* expert_offsets, const void* w2, void* out_sorted,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_combine - back to token order and weighted sum ([K3-ADD] moe_infer: the
+ * un-permute, the product with the routing weights in their fp32 precision,
+ * the sum over the k slots, the cast back).
+ *   y[n] = residual[n] + sum_{j = 0..k-1} topk_weight[n][j] *
+ *          out_sorted[inv_perm[n*k + j]],
+ *   accumulated in fp32 in that fixed j order, rounded once to dtype.
+ * out_sorted [N*k, d_in] dtype; inv_perm [N*k] int32; topk_weight [N, k] fp32;
+ * residual [N, d_in] dtype or NULL (zero).  Out: y [N, d_in] dtype.
+ * Needs no workspace.
+ */
+moe_status moe_combine(const moe_config* cfg, int64_t N, const void* out_sorted,
+                       const int32_t* inv_perm, const float* topk_weight, const void* residual,
+                       void* y, void* stream);
+
+/*
+ * moe_block_forward - the whole block ([K3-ADD] forward): route on the
+ * full-width hidden state; with d_latent > 0 project it down
+ * (x_in = hidden . w_down^T, rounded to dtype), else x_in = hidden; permute,
+ * gate/up, down and combine as above; with d_latent > 0 RMS-normalise each
+ * combined row in fp32 (y / sqrt(mean(y^2) + norm_eps) * gamma, when
+ * latent_norm) and project it up with w_up; with d_ff_shared > 0 add the
+ * shared expert (the same gated MLP and activation, on the full-width hidden)
+ * before the single final rounding.
+ * hidden [N, d] dtype.  Out: y [N, d] dtype.  Optional outputs (NULL skips):
+ * topk_idx_out [N, k] int32, topk_weight_out [N, k] fp32,
+ * tokens_per_expert_out [E] int32.
+ */
+moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights* w,
+                             const void* hidden, void* y, int32_t* topk_idx_out,
+                             float* topk_weight_out, int32_t* tokens_per_expert_out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_MOE_H */
