@@ -1,0 +1,238 @@
+"""Benchmark of the MoE block forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one moe_block_forward over one batch of synthetic tokens whose
+inputs are already resident in HBM (filled in place by the seeded device
+generator).  W untimed steps, then exactly K timed steps between device
+synchronisations; rank 0 prints one JSON line.  The default workload is the
+DeepSeek-V3-style prefill (4096 tokens, d 7168, 256 experts in 8 groups,
+top-4 groups, top-8, d_ff 2048, SiLU, bf16 experts, fp32 router).
+
+Beside the block throughput the line carries:
+  roofline      the dominant kernel (the routed gate/up grouped GEMM) timed with
+                HIP events recorded by libmoe on its own stream around that one
+                launch in every timed step; achieved = algorithmic bytes per launch
+                (active experts' w1 and w3, gathered input rows, h rows written)
+                / average launch time, against the 8 TB/s HBM peak;
+  cpu_baseline  the oracle (plain C, fp64) on the host's cores over a bounded
+                token sample of the same workload, as tokens/s.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + TFLOP/s (% bf16 MFMA peak); decode HBM GB/s (% peak)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+STAGES = ["route", "latent_down", "dispatch", "shared", "gate_up", "down", "combine"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="dsv3_prefill")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+class Hip:
+    """hipEvent helpers straight from the HIP runtime (events for libmoe's stage hooks)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        out = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+
+def algorithmic_work(w, counts):
+    """Flops and minimum bytes of one block forward, and of the gate/up launch."""
+    active = int((counts > 0).sum())
+    S = w.N * w.k
+    d_in = w.d_in
+    flops = 2.0 * S * 3 * d_in * w.d_ff + 6.0 * w.N * w.d * w.d_sh + 4.0 * w.N * w.d * w.L
+    router_flops = 2.0 * w.N * w.d * w.E
+    wbytes = active * 3 * d_in * w.d_ff * 2 + 3 * w.d * w.d_sh * 2 + 2 * w.d * w.L * 2
+    io = w.N * w.d * 2 * 2 + w.E * w.d * 4 + w.E * 4 + S * 8
+    gate_up_bytes = active * 2 * d_in * w.d_ff * 2 + S * d_in * 2 + S * w.d_ff * 2
+    return flops, router_flops, wbytes + io, gate_up_bytes, active
+
+
+def cpu_baseline(w, seconds):
+    """The oracle over a bounded token sample: router + experts + combine per token."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    x = synth.host_tensor(w, "hidden")
+    wr = synth.host_tensor(w, "w_router")
+    bias = synth.host_tensor(w, "bias")
+    n_tok = 8
+    toks = np.arange(0, w.N, w.N // n_tok)[:n_tok]
+    idx, wt, _ = oracle.route(x[toks], wr, bias, w.G, w.TG, w.k, w.norm_topk_prob, w.route_scale)
+    need = sorted({int(e) for e in idx.ravel()})
+    W = {n: {e: synth.host_tensor(w, n, expert=e) for e in need} for n in ("w1", "w3", "w2")}
+    for n in ("sh_w1", "sh_w3", "sh_w2", "w_down", "w_up", "gamma"):
+        if n in w.shapes():
+            W[n] = synth.host_tensor(w, n)
+    cfg = dict(d=w.d, E=w.E, k=w.k, d_ff=w.d_ff, d_sh=w.d_sh, L=w.L, act=w.act,
+               situ_beta=w.situ_beta, situ_linear_beta=w.situ_linear_beta,
+               latent_norm=w.latent_norm, norm_eps=w.norm_eps)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        i2, w2, _ = oracle.route(x[toks], wr, bias, w.G, w.TG, w.k, w.norm_topk_prob,
+                                 w.route_scale)
+        oracle.block_tokens(cfg, W, x[toks], np.arange(n_tok), i2, w2)
+        done += n_tok
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_tok} tokens of the same workload (every {w.N // n_tok}th), full router "
+                      f"+ their experts, repeated {done // n_tok}x over {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the expert-parallel design is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_29_amd as m
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    m.binding.lib()
+    w = synth.WORKLOADS[args.workload]
+    cfg = m.make_config(d=w.d, n_experts=w.E, n_group=w.G, topk_group=w.TG, top_k=w.k,
+                        d_ff=w.d_ff, route_scale=w.route_scale, norm_topk_prob=w.norm_topk_prob,
+                        act=w.act, situ_beta=w.situ_beta, situ_linear_beta=w.situ_linear_beta,
+                        d_latent=w.L, latent_norm=w.latent_norm, norm_eps=w.norm_eps,
+                        d_ff_shared=w.d_sh,
+                        dtype=m.DTYPE_BF16 if w.dtype == synth.BF16 else m.DTYPE_F32)
+    dev = {}
+    for name, shape in w.shapes().items():
+        dt = torch.float32 if w.dtype_of(name) == synth.F32 else torch.bfloat16
+        if name == "gamma" or (name == "bias" and w.bias_kind == "zipf"):
+            dev[name] = torch.from_numpy(synth.host_tensor(w, name)).cuda()
+        else:
+            dev[name] = torch.empty(shape, dtype=dt, device="cuda")
+            synth.fill_device(w, name, dev[name].data_ptr())
+    weights = m.Weights(w_router=dev["w_router"], bias=dev["bias"], w1=dev["w1"], w3=dev["w3"],
+                        w2=dev["w2"], w_down=dev.get("w_down"), gamma=dev.get("gamma"),
+                        w_up=dev.get("w_up"), sh_w1=dev.get("sh_w1"), sh_w3=dev.get("sh_w3"),
+                        sh_w2=dev.get("sh_w2"))
+    ydt = torch.bfloat16 if w.dtype == synth.BF16 else torch.float32
+    y = torch.empty((w.N, w.d), dtype=ydt, device="cuda")
+    counts = torch.empty((w.E,), dtype=torch.int32, device="cuda")
+    ws = m.workspace(cfg, w.N, m.CALL_BLOCK)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        m.moe_block_forward(cfg, w.N, weights, dev["hidden"], y, ws, tokens_per_expert_out=counts)
+    torch.cuda.synchronize()
+
+    hip = Hip()
+    n_ev = len(STAGES) + 1
+    events = [[hip.event() for _ in range(n_ev)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        arr = (ctypes.c_void_p * n_ev)(*[e.value for e in events[i]])
+        m.binding.lib().moe_set_stage_events(arr, n_ev)
+        m.moe_block_forward(cfg, w.N, weights, dev["hidden"], y, ws,
+                            tokens_per_expert_out=counts, stream=stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    m.binding.lib().moe_set_stage_events(None, 0)
+
+    stage_ms = {s: 0.0 for s in STAGES}
+    for i in range(args.steps):
+        for j, s in enumerate(STAGES):
+            stage_ms[s] += hip.elapsed_ms(events[i][j], events[i][j + 1]) / args.steps
+    ms_per_step = elapsed * 1e3 / args.steps
+    cnt = counts.cpu().numpy()
+    flops, router_flops, abytes, gu_bytes, active = algorithmic_work(w, cnt)
+    sec = ms_per_step / 1e3
+    gu_ms = stage_ms["gate_up"]
+    gu_gbs = gu_bytes / (gu_ms / 1e3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f).get(f"{w.name}/gate_up")
+        if tr:
+            traffic = tr.get("bytes_per_launch")
+    out = {
+        "metric": METRIC,
+        "value": w.N / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == synth.BF16 else "f32",
+        "data": "synthetic (seeded Philox normals; weights random, resident in HBM)",
+        "config": {"workload": w.name, "tokens": w.N, "B": w.B, "T": w.T, "d": w.d,
+                   "experts": w.E, "groups": w.G, "topk_group": w.TG, "top_k": w.k,
+                   "d_ff": w.d_ff, "d_ff_shared": w.d_sh, "d_latent": w.L, "act": w.act,
+                   "route_scale": w.route_scale, "parallelism": "single GPU"},
+        "tflops": flops / sec / 1e12,
+        "mfma_frac": flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "router_fp32_tflops": router_flops / sec / 1e12,
+        "hbm_gbs": abytes / sec / 1e9,
+        "hbm_frac": abytes / sec / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes": abytes,
+        "active_experts": active,
+        "tokens_per_expert": {"min": int(cnt.min()), "max": int(cnt.max()),
+                              "mean": float(cnt.mean())},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": {"kernel": "moe_gemm_bf16 (routed gate/up, gather, SiLU epilogue)",
+                     "bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gu_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_ms": gu_ms},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

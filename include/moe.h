@@ -222,6 +222,29 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
                              float* topk_weight_out, int32_t* tokens_per_expert_out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Tracing (no counterpart on the pages).  Stage boundaries of
+ * moe_block_forward at which, when set, an event is recorded on the call's
+ * stream, so that each stage's device time can be read with
+ * hipEventElapsedTime between consecutive events.
+ */
+typedef enum {
+  MOE_STAGE_BEGIN = 0,      /* before the router */
+  MOE_STAGE_ROUTED = 1,     /* after the router (weight split, logits, selection) */
+  MOE_STAGE_LATENT = 2,     /* after the latent down projection */
+  MOE_STAGE_DISPATCHED = 3, /* after mask, scan and scatter */
+  MOE_STAGE_SHARED = 4,     /* after the shared expert */
+  MOE_STAGE_GATE_UP = 5,    /* after the routed gate/up grouped GEMM */
+  MOE_STAGE_DOWN = 6,       /* after the routed down grouped GEMM */
+  MOE_STAGE_END = 7,        /* after combine (and norm + up projection) */
+  MOE_STAGE_COUNT = 8
+} moe_stage;
+
+/* Sets, for the calling thread, the MOE_STAGE_COUNT hipEvent_t handles that
+ * later moe_block_forward calls record (events = NULL clears them).  The
+ * events are owned by the caller and must stay valid while set. */
+moe_status moe_set_stage_events(void* const* events, int32_t n_events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,584 @@
+// api.cpp - the C ABI of libmoe (include/moe.h): host-side validation, the
+// workspace plan, and the order of kernel launches for each call.
+//
+// Every call validates on the host first and enqueues nothing on an error.
+// Launches go to the caller's stream in order; nothing here waits for the GPU
+// or allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_stage_events[MOE_STAGE_COUNT];
+thread_local bool g_stage_events_set = false;
+
+hipError_t mark(int stage, hipStream_t s) {
+  if (!g_stage_events_set) return hipSuccess;
+  return hipEventRecord(g_stage_events[stage], s);
+}
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                                     \
+  do {                                                                                     \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);        \
+    if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+#define CHECK_HIP(expr)                                                                    \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess)                                                                  \
+      return fail(MOE_ERR_HIP, "%s: %s failed: %s", fn, #expr, hipGetErrorString(e_));     \
+  } while (0)
+
+int64_t d_in_of(const moe_config* c) { return c->d_latent > 0 ? c->d_latent : c->d; }
+size_t esize(const moe_config* c) { return c->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+bool is_bf16(const moe_config* c) { return c->dtype == MOE_DTYPE_BF16; }
+
+constexpr int64_t kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int64_t kMaxLatent = 16384;  // row width of the fused combine + RMS norm
+
+moe_status validate(const moe_config* c, const char* fn) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "%s: cfg is NULL", fn);
+  if (c->training) return fail(MOE_ERR_UNSUPPORTED, "%s: training mode is not supported", fn);
+  if (c->score_func != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: scoring function %d is not supported (sigmoid only)", fn,
+                c->score_func);
+  if (c->topk_method != MOE_TOPK_NOAUX_TC)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: top-k method %d is not supported (noaux_tc only)", fn,
+                c->topk_method);
+  if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: dtype %d is not supported", fn, c->dtype);
+  if (c->act != MOE_ACT_SILU && c->act != MOE_ACT_SITU)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: activation %d is not supported", fn, c->act);
+  if (c->d <= 0 || c->d % 8) return fail(MOE_ERR_INVALID_ARG, "%s: d=%lld must be a positive multiple of 8", fn, (long long)c->d);
+  if (c->d_ff <= 0 || c->d_ff % 8) return fail(MOE_ERR_INVALID_ARG, "%s: d_ff=%lld must be a positive multiple of 8", fn, (long long)c->d_ff);
+  if (c->d_latent < 0 || c->d_latent % 8) return fail(MOE_ERR_INVALID_ARG, "%s: d_latent=%lld must be 0 or a positive multiple of 8", fn, (long long)c->d_latent);
+  if (c->d_latent > kMaxLatent) return fail(MOE_ERR_UNSUPPORTED, "%s: d_latent=%lld exceeds %lld", fn, (long long)c->d_latent, (long long)kMaxLatent);
+  if (c->d_ff_shared < 0 || c->d_ff_shared % 8) return fail(MOE_ERR_INVALID_ARG, "%s: d_ff_shared=%lld must be 0 or a positive multiple of 8", fn, (long long)c->d_ff_shared);
+  if (c->n_experts < 2) return fail(MOE_ERR_INVALID_ARG, "%s: n_experts=%lld must be >= 2", fn, (long long)c->n_experts);
+  if (c->n_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "%s: n_experts=%lld exceeds %lld", fn, (long long)c->n_experts, (long long)kMaxExperts);
+  if (c->n_group < 1 || c->n_experts % c->n_group)
+    return fail(MOE_ERR_INVALID_ARG, "%s: n_group=%d must divide n_experts=%lld", fn, c->n_group, (long long)c->n_experts);
+  const int64_t per = c->n_experts / c->n_group;
+  if (per < 2) return fail(MOE_ERR_INVALID_ARG, "%s: groups need at least 2 experts (E/G=%lld)", fn, (long long)per);
+  if (c->topk_group < 1 || c->topk_group > c->n_group)
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_group=%d must be in [1, n_group=%d]", fn, c->topk_group, c->n_group);
+  if (c->top_k < 1 || c->top_k > (int64_t)c->topk_group * per)
+    return fail(MOE_ERR_INVALID_ARG, "%s: top_k=%d must be in [1, topk_group*E/G=%lld]", fn, c->top_k, (long long)(c->topk_group * per));
+  if (c->top_k > kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "%s: top_k=%d exceeds %d", fn, c->top_k, kMaxTopK);
+  if (!std::isfinite(c->route_scale)) return fail(MOE_ERR_INVALID_ARG, "%s: route_scale is not finite", fn);
+  if (c->act == MOE_ACT_SITU) {
+    if (!std::isfinite(c->situ_beta) || c->situ_beta < 0.0f)
+      return fail(MOE_ERR_INVALID_ARG, "%s: situ_beta must be finite and >= 0", fn);
+    if (!std::isfinite(c->situ_linear_beta)) return fail(MOE_ERR_INVALID_ARG, "%s: situ_linear_beta is not finite", fn);
+  }
+  if (c->d_latent > 0 && (!std::isfinite(c->norm_eps) || c->norm_eps < 0.0f))
+    return fail(MOE_ERR_INVALID_ARG, "%s: norm_eps must be finite and >= 0", fn);
+  return MOE_OK;
+}
+
+moe_status validate_n(const moe_config* c, int64_t N, const char* fn) {
+  if (N < 0) return fail(MOE_ERR_INVALID_ARG, "%s: N=%lld is negative", fn, (long long)N);
+  if (N * (int64_t)c->top_k > INT32_MAX || N > INT32_MAX / 64)
+    return fail(MOE_ERR_INVALID_ARG, "%s: N=%lld is too large (N*k must fit int32)", fn, (long long)N);
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace plan.
+struct Plan {
+  size_t bytes = 0;
+  size_t w_split = 0, logits = 0, idx = 0, wts = 0, bits = 0, base = 0, counts = 0, offsets = 0;
+  size_t mt_off = 0, tile_seg = 0, perm = 0, inv_perm = 0, x_lat = 0, h = 0, out = 0;
+  size_t sh_h = 0, sh_out = 0, y_lat = 0;
+  int rb = 4;              // row blocks of 32 per grouped-GEMM tile (bf16)
+  int rows_per_tile = 128; // rows per grouped-GEMM m-tile
+  int64_t tile_cap = 0;
+  int64_t dp = 0;          // router width padded to 64
+  int64_t n_chunks = 0;
+};
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t b) {
+    const size_t at = off;
+    off += (b + 255) & ~size_t(255);
+    return at;
+  }
+};
+
+int choose_rb(const moe_config* c, int64_t N) {
+  const double avg = (double)N * c->top_k / (double)c->n_experts;
+  if (avg >= 80.0) return 4;
+  if (avg >= 24.0) return 2;
+  return 1;
+}
+
+int dense_rb(int64_t rows) {
+  if (rows >= 2048) return 4;
+  if (rows >= 512) return 2;
+  return 1;
+}
+
+Plan make_plan(const moe_config* c, int64_t N, int call) {
+  Plan p;
+  const int64_t E = c->n_experts, k = c->top_k, S = N * k;
+  const size_t es = esize(c);
+  p.rb = choose_rb(c, N);
+  p.rows_per_tile = is_bf16(c) ? p.rb * 32 : moe::gemm_f32_rows_per_tile();
+  p.tile_cap = S / p.rows_per_tile + (E < S ? E : S) + 1;
+  p.dp = (c->d + 63) / 64 * 64;
+  p.n_chunks = (N + 63) / 64;
+  Carver cv;
+  const bool block = call == MOE_CALL_BLOCK;
+  if (call == MOE_CALL_ROUTE || block) {
+    if (is_bf16(c)) p.w_split = cv.take((size_t)E * 3 * p.dp * 2);
+    p.logits = cv.take((size_t)N * E * 4);
+  }
+  if (call == MOE_CALL_PERMUTE || block) {
+    p.bits = cv.take((size_t)p.n_chunks * E * 8);
+    p.base = cv.take((size_t)p.n_chunks * E * 4);
+  }
+  if (call == MOE_CALL_GATE_UP || call == MOE_CALL_DOWN || block) {
+    p.mt_off = cv.take((size_t)(E + 1) * 4);
+    p.tile_seg = cv.take((size_t)p.tile_cap * 4);
+  }
+  if (block) {
+    const int64_t d_in = d_in_of(c);
+    p.idx = cv.take((size_t)S * 4);
+    p.wts = cv.take((size_t)S * 4);
+    p.counts = cv.take((size_t)E * 4);
+    p.offsets = cv.take((size_t)(E + 1) * 4);
+    p.perm = cv.take((size_t)S * 4);
+    p.inv_perm = cv.take((size_t)S * 4);
+    p.h = cv.take((size_t)S * c->d_ff * es);
+    p.out = cv.take((size_t)S * d_in * es);
+    if (c->d_latent > 0) {
+      p.x_lat = cv.take((size_t)N * c->d_latent * es);
+      p.y_lat = cv.take((size_t)N * c->d_latent * es);
+    }
+    if (c->d_ff_shared > 0) {
+      p.sh_h = cv.take((size_t)N * c->d_ff_shared * es);
+      p.sh_out = cv.take((size_t)N * c->d * es);
+    }
+  }
+  p.bytes = cv.off;
+  return p;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe_status check_ws(const Plan& p, void* ws, size_t ws_bytes, const char* fn) {
+  if (p.bytes == 0) return MOE_OK;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, p.bytes);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace is not 256-byte aligned", fn);
+  if (ws_bytes < p.bytes)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes, p.bytes);
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Launch sequences (arguments already validated).
+
+moe::GemmArgs gemm_args() {
+  moe::GemmArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.a_div = 1;
+  a.beta = 1.0f;
+  return a;
+}
+
+hipError_t dense_gemm(const moe_config* c, const void* A, int64_t rows, int64_t K, const void* B0,
+                      const void* B1, int64_t n_cols, void* C, int epi, const void* residual,
+                      hipStream_t s) {
+  moe::GemmArgs a = gemm_args();
+  a.A = A;
+  a.lda = K;
+  a.a_rows = rows;
+  a.B0 = B0;
+  a.B1 = B1;
+  a.K = K;
+  a.n_cols = n_cols;
+  a.dense_rows = rows;
+  a.C = C;
+  a.ldc = n_cols;
+  a.c_rows = rows;
+  a.residual = residual;
+  a.ld_res = n_cols;
+  a.act = c->act;
+  a.beta = c->situ_beta > 0.0f ? c->situ_beta : 1.0f;
+  a.lbeta = c->situ_linear_beta;
+  if (is_bf16(c)) return moe::launch_gemm_bf16(a, epi, moe::A_DIRECT, dense_rb(rows), 0, s);
+  return moe::launch_gemm_f32(a, epi, moe::A_DIRECT, 0, s);
+}
+
+hipError_t grouped_gemm(const moe_config* c, const Plan& p, int64_t N, const void* A, int amode,
+                        const int32_t* a_map, int64_t a_rows, int64_t K, const int32_t* seg_off,
+                        const void* B0, const void* B1, int64_t n_cols, void* C, int epi,
+                        void* ws, hipStream_t s) {
+  moe::GemmArgs a = gemm_args();
+  a.A = A;
+  a.lda = K;
+  a.a_map = a_map;
+  a.a_div = c->top_k;
+  a.a_rows = a_rows;
+  a.B0 = B0;
+  a.B1 = B1;
+  a.b_seg_stride = n_cols * K;
+  a.K = K;
+  a.n_cols = n_cols;
+  a.seg_off = seg_off;
+  a.mt_off = at<int32_t>(ws, p.mt_off);
+  a.tile_seg = at<int32_t>(ws, p.tile_seg);
+  a.tile_cap = p.tile_cap;
+  a.C = C;
+  a.ldc = n_cols;
+  a.c_rows = N * c->top_k;
+  a.act = c->act;
+  a.beta = c->situ_beta > 0.0f ? c->situ_beta : 1.0f;
+  a.lbeta = c->situ_linear_beta;
+  if (is_bf16(c)) return moe::launch_gemm_bf16(a, epi, amode, p.rb, p.tile_cap, s);
+  return moe::launch_gemm_f32(a, epi, amode, p.tile_cap, s);
+}
+
+moe_status run_route(const moe_config* c, int64_t N, const void* hidden, const float* w_router,
+                     const float* bias, int32_t* idx, float* wts, void* ws, const Plan& p,
+                     hipStream_t s, const char* fn) {
+  const int64_t E = c->n_experts;
+  float* logits = at<float>(ws, p.logits);
+  if (is_bf16(c)) {
+    moe::bf16_t* split = at<moe::bf16_t>(ws, p.w_split);
+    CHECK_HIP(moe::launch_router_split(w_router, E, c->d, p.dp, split, s));
+    moe::GemmArgs a = gemm_args();
+    a.A = hidden;
+    a.lda = c->d;
+    a.a_rows = N;
+    a.a_period = p.dp;
+    a.a_valid = c->d;
+    a.B0 = split;
+    a.K = 3 * p.dp;
+    a.n_cols = E;
+    a.dense_rows = N;
+    a.C = logits;
+    a.ldc = E;
+    a.c_rows = N;
+    CHECK_HIP(moe::launch_gemm_bf16(a, moe::EPI_STORE_F32, moe::A_REPEAT, dense_rb(N), 0, s));
+  } else {
+    CHECK_HIP(dense_gemm(c, hidden, N, c->d, w_router, nullptr, E, logits, moe::EPI_STORE, nullptr, s));
+  }
+  CHECK_HIP(moe::launch_route_select(logits, bias, N, E, c->n_group, c->topk_group, c->top_k,
+                                     c->norm_topk_prob ? 1 : 0, c->route_scale, idx, wts, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_validate_config(const moe_config* cfg) {
+  moe_status st = validate(cfg, "moe_validate_config");
+  return st == MOE_OK ? ok() : st;
+}
+
+moe_status moe_workspace_size(const moe_config* cfg, int64_t N, int32_t call, size_t* bytes) {
+  const char* fn = "moe_workspace_size";
+  moe_status st = validate(cfg, fn);
+  if (st != MOE_OK) return st;
+  if ((st = validate_n(cfg, N, fn)) != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  if (call < MOE_CALL_ROUTE || call > MOE_CALL_BLOCK) return fail(MOE_ERR_INVALID_ARG, "%s: unknown call %d", fn, call);
+  *bytes = make_plan(cfg, N, call).bytes;
+  return ok();
+}
+
+moe_status moe_route(const moe_config* cfg, int64_t N, const void* hidden, const float* w_router,
+                     const float* bias, int32_t* topk_idx, float* topk_weight, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_route";
+  moe_status st = validate(cfg, fn);
+  if (st != MOE_OK) return st;
+  if ((st = validate_n(cfg, N, fn)) != MOE_OK) return st;
+  if (N == 0) return ok();
+  REQUIRE_PTR(hidden);
+  REQUIRE_PTR(w_router);
+  REQUIRE_PTR(bias);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(topk_weight);
+  const Plan p = make_plan(cfg, N, MOE_CALL_ROUTE);
+  if ((st = check_ws(p, workspace, workspace_bytes, fn)) != MOE_OK) return st;
+  st = run_route(cfg, N, hidden, w_router, bias, topk_idx, topk_weight, workspace, p,
+                 static_cast<hipStream_t>(stream), fn);
+  return st == MOE_OK ? ok() : st;
+}
+
+moe_status moe_permute(const moe_config* cfg, int64_t N, const int32_t* topk_idx, const void* x_in,
+                       int32_t* tokens_per_expert, int32_t* expert_offsets, int32_t* perm,
+                       int32_t* inv_perm, void* x_sorted, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  const char* fn = "moe_permute";
+  moe_status st = validate(cfg, fn);
+  if (st != MOE_OK) return st;
+  if ((st = validate_n(cfg, N, fn)) != MOE_OK) return st;
+  REQUIRE_PTR(tokens_per_expert);
+  REQUIRE_PTR(expert_offsets);
+  if (N > 0) {
+    REQUIRE_PTR(topk_idx);
+    REQUIRE_PTR(perm);
+    REQUIRE_PTR(inv_perm);
+    if (x_sorted) {
+      REQUIRE_PTR(x_in);
+      REQUIRE_PTR(x_sorted);
+    }
+  }
+  const Plan p = make_plan(cfg, N, MOE_CALL_PERMUTE);
+  if ((st = check_ws(p, workspace, workspace_bytes, fn)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t E = cfg->n_experts;
+  const int k = cfg->top_k;
+  uint64_t* bits = at<uint64_t>(workspace, p.bits);
+  int32_t* base = at<int32_t>(workspace, p.base);
+  CHECK_HIP(moe::launch_dispatch_mask(topk_idx, N, k, E, bits, s));
+  CHECK_HIP(moe::launch_dispatch_scan(bits, p.n_chunks, E, tokens_per_expert, expert_offsets, base,
+                                      0, nullptr, nullptr, 0, s));
+  CHECK_HIP(moe::launch_dispatch_scatter(topk_idx, N, k, E, bits, base, perm, inv_perm, s));
+  if (x_sorted && N > 0)
+    CHECK_HIP(moe::launch_gather_rows(x_in, N, d_in_of(cfg), (int)esize(cfg), perm, k, N * k,
+                                      x_sorted, s));
+  return ok();
+}
+
+static moe_status expert_call(const moe_config* cfg, int64_t N, const void* A,
+                              const int32_t* expert_offsets, const void* B0, const void* B1,
+                              void* C, void* workspace, size_t workspace_bytes, void* stream,
+                              bool gate_up, const char* fn) {
+  moe_status st = validate(cfg, fn);
+  if (st != MOE_OK) return st;
+  if ((st = validate_n(cfg, N, fn)) != MOE_OK) return st;
+  if (N == 0) return ok();
+  REQUIRE_PTR(A);
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(B0);
+  if (gate_up) REQUIRE_PTR(B1);
+  REQUIRE_PTR(C);
+  const Plan p = make_plan(cfg, N, gate_up ? MOE_CALL_GATE_UP : MOE_CALL_DOWN);
+  if ((st = check_ws(p, workspace, workspace_bytes, fn)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CHECK_HIP(moe::launch_tiles_from_offsets(expert_offsets, cfg->n_experts, p.rows_per_tile,
+                                           at<int32_t>(workspace, p.mt_off),
+                                           at<int32_t>(workspace, p.tile_seg), p.tile_cap, s));
+  const int64_t d_in = d_in_of(cfg);
+  if (gate_up) {
+    CHECK_HIP(grouped_gemm(cfg, p, N, A, moe::A_DIRECT, nullptr, N * cfg->top_k, d_in,
+                           expert_offsets, B0, B1, cfg->d_ff, C, moe::EPI_GATE_UP, workspace, s));
+  } else {
+    CHECK_HIP(grouped_gemm(cfg, p, N, A, moe::A_DIRECT, nullptr, N * cfg->top_k, cfg->d_ff,
+                           expert_offsets, B0, nullptr, d_in, C, moe::EPI_STORE, workspace, s));
+  }
+  return ok();
+}
+
+moe_status moe_expert_gate_up(const moe_config* cfg, int64_t N, const void* x_sorted,
+                              const int32_t* expert_offsets, const void* w1, const void* w3,
+                              void* h_sorted, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return expert_call(cfg, N, x_sorted, expert_offsets, w1, w3, h_sorted, workspace,
+                     workspace_bytes, stream, true, "moe_expert_gate_up");
+}
+
+moe_status moe_expert_down(const moe_config* cfg, int64_t N, const void* h_sorted,
+                           const int32_t* expert_offsets, const void* w2, void* out_sorted,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return expert_call(cfg, N, h_sorted, expert_offsets, w2, nullptr, out_sorted, workspace,
+                     workspace_bytes, stream, false, "moe_expert_down");
+}
+
+moe_status moe_combine(const moe_config* cfg, int64_t N, const void* out_sorted,
+                       const int32_t* inv_perm, const float* topk_weight, const void* residual,
+                       void* y, void* stream) {
+  const char* fn = "moe_combine";
+  moe_status st = validate(cfg, fn);
+  if (st != MOE_OK) return st;
+  if ((st = validate_n(cfg, N, fn)) != MOE_OK) return st;
+  if (N == 0) return ok();
+  REQUIRE_PTR(out_sorted);
+  REQUIRE_PTR(inv_perm);
+  REQUIRE_PTR(topk_weight);
+  REQUIRE_PTR(y);
+  if (residual && !aligned16(residual))
+    return fail(MOE_ERR_INVALID_ARG, "%s: residual is not 16-byte aligned", fn);
+  CHECK_HIP(moe::launch_combine(out_sorted, inv_perm, topk_weight, residual, y, N, cfg->top_k,
+                                d_in_of(cfg), N * cfg->top_k, is_bf16(cfg) ? 1 : 0,
+                                static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights* w,
+                             const void* hidden, void* y, int32_t* topk_idx_out,
+                             float* topk_weight_out, int32_t* tokens_per_expert_out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_block_forward";
+  moe_status st = validate(cfg, fn);
+  if (st != MOE_OK) return st;
+  if ((st = validate_n(cfg, N, fn)) != MOE_OK) return st;
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "%s: w is NULL", fn);
+  if (N == 0) return ok();
+  REQUIRE_PTR(hidden);
+  REQUIRE_PTR(y);
+  REQUIRE_PTR(w->w_router);
+  REQUIRE_PTR(w->bias);
+  REQUIRE_PTR(w->w1);
+  REQUIRE_PTR(w->w3);
+  REQUIRE_PTR(w->w2);
+  if (cfg->d_latent > 0) {
+    REQUIRE_PTR(w->w_down);
+    REQUIRE_PTR(w->w_up);
+    if (cfg->latent_norm) REQUIRE_PTR(w->gamma);
+  }
+  if (cfg->d_ff_shared > 0) {
+    REQUIRE_PTR(w->sh_w1);
+    REQUIRE_PTR(w->sh_w3);
+    REQUIRE_PTR(w->sh_w2);
+  }
+  if (topk_idx_out && !aligned16(topk_idx_out))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_idx_out is not 16-byte aligned", fn);
+  if (topk_weight_out && !aligned16(topk_weight_out))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_weight_out is not 16-byte aligned", fn);
+  if (tokens_per_expert_out && !aligned16(tokens_per_expert_out))
+    return fail(MOE_ERR_INVALID_ARG, "%s: tokens_per_expert_out is not 16-byte aligned", fn);
+  const Plan p = make_plan(cfg, N, MOE_CALL_BLOCK);
+  if ((st = check_ws(p, workspace, workspace_bytes, fn)) != MOE_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = workspace;
+  const int64_t E = cfg->n_experts, k = cfg->top_k, S = N * k;
+  const int64_t d = cfg->d, L = cfg->d_latent, d_in = d_in_of(cfg);
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, p.idx);
+  float* wts = topk_weight_out ? topk_weight_out : at<float>(ws, p.wts);
+  int32_t* counts = tokens_per_expert_out ? tokens_per_expert_out : at<int32_t>(ws, p.counts);
+  int32_t* offsets = at<int32_t>(ws, p.offsets);
+  int32_t* perm = at<int32_t>(ws, p.perm);
+  int32_t* inv = at<int32_t>(ws, p.inv_perm);
+
+  // router on the full-width input
+  CHECK_HIP(mark(MOE_STAGE_BEGIN, s));
+  st = run_route(cfg, N, hidden, w->w_router, w->bias, idx, wts, ws, p, s, fn);
+  if (st != MOE_OK) return st;
+  CHECK_HIP(mark(MOE_STAGE_ROUTED, s));
+
+  // latent down projection
+  const void* x_in = hidden;
+  if (L > 0) {
+    void* x_lat = at<void>(ws, p.x_lat);
+    CHECK_HIP(dense_gemm(cfg, hidden, N, d, w->w_down, nullptr, L, x_lat, moe::EPI_STORE, nullptr, s));
+    x_in = x_lat;
+  }
+  CHECK_HIP(mark(MOE_STAGE_LATENT, s));
+
+  // dispatch
+  uint64_t* bits = at<uint64_t>(ws, p.bits);
+  int32_t* base = at<int32_t>(ws, p.base);
+  CHECK_HIP(moe::launch_dispatch_mask(idx, N, (int)k, E, bits, s));
+  CHECK_HIP(moe::launch_dispatch_scan(bits, p.n_chunks, E, counts, offsets, base, p.rows_per_tile,
+                                      at<int32_t>(ws, p.mt_off), at<int32_t>(ws, p.tile_seg),
+                                      p.tile_cap, s));
+  CHECK_HIP(moe::launch_dispatch_scatter(idx, N, (int)k, E, bits, base, perm, inv, s));
+  CHECK_HIP(mark(MOE_STAGE_DISPATCHED, s));
+
+  // shared expert on the full-width input
+  void* sh_out = nullptr;
+  if (cfg->d_ff_shared > 0) {
+    void* sh_h = at<void>(ws, p.sh_h);
+    sh_out = at<void>(ws, p.sh_out);
+    CHECK_HIP(dense_gemm(cfg, hidden, N, d, w->sh_w1, w->sh_w3, cfg->d_ff_shared, sh_h,
+                         moe::EPI_GATE_UP, nullptr, s));
+    CHECK_HIP(dense_gemm(cfg, sh_h, N, cfg->d_ff_shared, w->sh_w2, nullptr, d, sh_out,
+                         moe::EPI_STORE, nullptr, s));
+  }
+
+  CHECK_HIP(mark(MOE_STAGE_SHARED, s));
+
+  // routed experts: rows gathered through the permutation
+  void* h = at<void>(ws, p.h);
+  void* out = at<void>(ws, p.out);
+  CHECK_HIP(grouped_gemm(cfg, p, N, x_in, moe::A_GATHER, perm, N, d_in, offsets, w->w1, w->w3,
+                         cfg->d_ff, h, moe::EPI_GATE_UP, ws, s));
+  CHECK_HIP(mark(MOE_STAGE_GATE_UP, s));
+  CHECK_HIP(grouped_gemm(cfg, p, N, h, moe::A_DIRECT, nullptr, S, cfg->d_ff, offsets, w->w2,
+                         nullptr, d_in, out, moe::EPI_STORE, ws, s));
+  CHECK_HIP(mark(MOE_STAGE_DOWN, s));
+
+  if (L > 0) {
+    void* y_lat = at<void>(ws, p.y_lat);
+    CHECK_HIP(moe::launch_combine_rmsnorm(out, inv, wts, w->gamma, cfg->norm_eps,
+                                          cfg->latent_norm ? 1 : 0, y_lat, N, (int)k, L, S,
+                                          is_bf16(cfg) ? 1 : 0, s));
+    CHECK_HIP(dense_gemm(cfg, y_lat, N, L, w->w_up, nullptr, d, y,
+                         sh_out ? moe::EPI_STORE_RES : moe::EPI_STORE, sh_out, s));
+  } else {
+    CHECK_HIP(moe::launch_combine(out, inv, wts, sh_out, y, N, (int)k, d, S, is_bf16(cfg) ? 1 : 0, s));
+  }
+  CHECK_HIP(mark(MOE_STAGE_END, s));
+  return ok();
+}
+
+moe_status moe_set_stage_events(void* const* events, int32_t n_events) {
+  const char* fn = "moe_set_stage_events";
+  if (!events) {
+    g_stage_events_set = false;
+    return ok();
+  }
+  if (n_events != MOE_STAGE_COUNT)
+    return fail(MOE_ERR_INVALID_ARG, "%s: %d events given, %d needed", fn, n_events, (int)MOE_STAGE_COUNT);
+  for (int i = 0; i < MOE_STAGE_COUNT; ++i) {
+    if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "%s: event %d is NULL", fn, i);
+    g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  g_stage_events_set = true;
+  return ok();
+}
+
+}  // extern "C"

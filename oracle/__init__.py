@@ -83,6 +83,12 @@ def _load():
         lib.oracle_block_tokens.argtypes = [ctypes.POINTER(_BlockCfg),
                                             ctypes.POINTER(_BlockWeights), P, i64, P, P, P, P]
         lib.oracle_block_tokens.restype = i32
+        lib.oracle_gate_up_rows.argtypes = [ctypes.POINTER(_BlockCfg), P, P, i64, P, P, P]
+        lib.oracle_gate_up_rows.restype = i32
+        lib.oracle_down_rows.argtypes = [ctypes.POINTER(_BlockCfg), P, i64, P, P, P]
+        lib.oracle_down_rows.restype = i32
+        lib.oracle_combine.argtypes = [i64, i32, i64, i32, P, P, P, P, P]
+        lib.oracle_combine.restype = i32
         _lib = lib
     return _lib
 
@@ -244,6 +250,74 @@ def block_tokens(cfg: dict, weights_: dict, x, tokens, topk_idx, topk_weight):
                                      y.ctypes.data)
     if rc:
         raise RuntimeError(f"oracle_block_tokens failed ({rc})")
+    return y
+
+
+def _cfg_struct(cfg: dict, dt: int) -> _BlockCfg:
+    return _BlockCfg(d=int(cfg["d"]), E=int(cfg["E"]), k=int(cfg.get("k", 1)),
+                     d_ff=int(cfg["d_ff"]), d_sh=int(cfg.get("d_sh", 0)), L=int(cfg.get("L", 0)),
+                     act=ACT[cfg.get("act", "silu")], situ_beta=float(cfg.get("situ_beta", 1.0)),
+                     situ_linear_beta=float(cfg.get("situ_linear_beta", 0.0)),
+                     latent_norm=int(bool(cfg.get("latent_norm", True))),
+                     norm_eps=float(cfg.get("norm_eps", 1e-6)), dtype=dt)
+
+
+def _ptr_table(src, E, keep):
+    arr = (ctypes.c_void_p * E)()
+    for e in range(E):
+        m = src.get(e) if isinstance(src, dict) else src[e]
+        if m is not None:
+            m = _c(m)
+            keep.append(m)
+            arr[e] = m.ctypes.data
+    keep.append(arr)
+    return arr
+
+
+def gate_up_rows(cfg: dict, w1, w3, x_rows, expert):
+    """h [R, d_ff] fp64: act(w1[e] x, w3[e] x) for each row x with its expert e."""
+    x_rows = _c(x_rows)
+    expert = _c(np.asarray(expert), np.int32)
+    R = x_rows.shape[0]
+    keep = []
+    c = _cfg_struct(cfg, _dtype_code(x_rows))
+    h = np.empty((R, c.d_ff), np.float64)
+    rc = _load().oracle_gate_up_rows(ctypes.byref(c), _ptr_table(w1, c.E, keep),
+                                     _ptr_table(w3, c.E, keep), R, x_rows.ctypes.data,
+                                     expert.ctypes.data, h.ctypes.data)
+    if rc:
+        raise RuntimeError(f"oracle_gate_up_rows failed ({rc})")
+    return h
+
+
+def down_rows(cfg: dict, w2, h_rows, expert):
+    """out [R, d_in] fp64: w2[e] h for each row h with its expert e."""
+    h_rows = _c(h_rows)
+    expert = _c(np.asarray(expert), np.int32)
+    R = h_rows.shape[0]
+    keep = []
+    c = _cfg_struct(cfg, _dtype_code(h_rows))
+    d_in = c.L or c.d
+    out = np.empty((R, d_in), np.float64)
+    rc = _load().oracle_down_rows(ctypes.byref(c), _ptr_table(w2, c.E, keep), R,
+                                  h_rows.ctypes.data, expert.ctypes.data, out.ctypes.data)
+    if rc:
+        raise RuntimeError(f"oracle_down_rows failed ({rc})")
+    return out
+
+
+def combine(out_sorted, inv_perm, topk_weight, residual=None):
+    """y [N, width] fp64 = residual + sum_j w[n, j] * out_sorted[inv_perm[n*k + j]]."""
+    out_sorted = _c(out_sorted)
+    w = _c(topk_weight, np.float32)
+    N, k = w.shape
+    inv = _c(np.asarray(inv_perm).reshape(-1), np.int32)
+    width = out_sorted.shape[1]
+    res = None if residual is None else _c(residual)
+    y = np.empty((N, width), np.float64)
+    _load().oracle_combine(N, k, width, _dtype_code(out_sorted), out_sorted.ctypes.data,
+                           inv.ctypes.data, w.ctypes.data,
+                           None if res is None else res.ctypes.data, y.ctypes.data)
     return y
 
 

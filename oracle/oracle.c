@@ -284,11 +284,11 @@ static double act_pair(const oracle_block_cfg* c, double g, double u) {
   return a * u;
 }
 
-/* o[d_out] = w2 act(w1 v, w3 v) for one row v[d_model], with w1, w3 stored
+/* The two halves of one gated MLP for one row, with w1, w3 stored
  * [d_hidden, d_model] and w2 stored [d_model, d_hidden] (nn.Linear [out, in],
- * no bias - [K3-GATE] expert). */
-static void gated_mlp(const oracle_block_cfg* c, const void* w1, const void* w3, const void* w2,
-                      int64_t d_model, int64_t d_hidden, const double* v, double* h, double* o) {
+ * no bias - [K3-GATE] expert):  h = act(w1 v, w3 v),  o = w2 h. */
+static void gate_up_vec(const oracle_block_cfg* c, const void* w1, const void* w3, int64_t d_model,
+                        int64_t d_hidden, const double* v, double* h) {
   for (int64_t i = 0; i < d_hidden; ++i) {
     double g = 0.0, u = 0.0;
     for (int64_t t = 0; t < d_model; ++t) {
@@ -297,11 +297,83 @@ static void gated_mlp(const oracle_block_cfg* c, const void* w1, const void* w3,
     }
     h[i] = act_pair(c, g, u);
   }
+}
+
+static void down_vec(const oracle_block_cfg* c, const void* w2, int64_t d_model, int64_t d_hidden,
+                     const double* h, double* o) {
   for (int64_t t = 0; t < d_model; ++t) {
     double acc = 0.0;
     for (int64_t i = 0; i < d_hidden; ++i) acc += elem(w2, c->dtype, t * d_hidden + i) * h[i];
     o[t] = acc;
   }
+}
+
+static void gated_mlp(const oracle_block_cfg* c, const void* w1, const void* w3, const void* w2,
+                      int64_t d_model, int64_t d_hidden, const double* v, double* h, double* o) {
+  gate_up_vec(c, w1, w3, d_model, d_hidden, v, h);
+  down_vec(c, w2, d_model, d_hidden, h, o);
+}
+
+/* Per-row halves on given rows (each row with its expert), for checking the
+ * expert calls on their own: h[r] = act(w1[e] x[r], w3[e] x[r]) and
+ * out[r] = w2[e] h[r], fp64, with x and h rows of the block's element type. */
+int oracle_gate_up_rows(const oracle_block_cfg* c, const void* const* w1, const void* const* w3,
+                        int64_t R, const void* x_rows, const int32_t* expert, double* h) {
+  const int64_t d_in = c->L ? c->L : c->d;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(+ : bad)
+  for (int64_t r = 0; r < R; ++r) {
+    const int32_t e = expert[r];
+    double* v = (double*)malloc(sizeof(double) * (size_t)d_in);
+    if (!v || e < 0 || e >= c->E || !w1[e] || !w3[e]) {
+      free(v);
+      ++bad;
+      continue;
+    }
+    for (int64_t t = 0; t < d_in; ++t) v[t] = elem(x_rows, c->dtype, r * d_in + t);
+    gate_up_vec(c, w1[e], w3[e], d_in, c->d_ff, v, h + r * c->d_ff);
+    free(v);
+  }
+  return bad ? 2 : 0;
+}
+
+int oracle_down_rows(const oracle_block_cfg* c, const void* const* w2, int64_t R,
+                     const void* h_rows, const int32_t* expert, double* out) {
+  const int64_t d_in = c->L ? c->L : c->d;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(+ : bad)
+  for (int64_t r = 0; r < R; ++r) {
+    const int32_t e = expert[r];
+    double* h = (double*)malloc(sizeof(double) * (size_t)c->d_ff);
+    if (!h || e < 0 || e >= c->E || !w2[e]) {
+      free(h);
+      ++bad;
+      continue;
+    }
+    for (int64_t t = 0; t < c->d_ff; ++t) h[t] = elem(h_rows, c->dtype, r * c->d_ff + t);
+    down_vec(c, w2[e], d_in, c->d_ff, h, out + r * d_in);
+    free(h);
+  }
+  return bad ? 2 : 0;
+}
+
+/* [K3-ADD] moe_infer, last step: new_x[idxs] = outs un-permutes the expert
+ * rows; the k rows of a token are multiplied by their routing weights and
+ * summed; here in fp64, plus an optional residual row. */
+int oracle_combine(int64_t N, int k, int64_t width, int dtype, const void* out_sorted,
+                   const int32_t* inv_perm, const float* w, const void* residual, double* y) {
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t c = 0; c < width; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) {
+        const int64_t p = inv_perm[n * k + j];
+        acc += (double)w[n * k + j] * elem(out_sorted, dtype, p * width + c);
+      }
+      if (residual) acc += elem(residual, dtype, n * width + c);
+      y[n * width + c] = acc;
+    }
+  }
+  return 0;
 }
 
 /* [K3-ADD] forward: the router scores the full-width input; with the latent

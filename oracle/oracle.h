@@ -101,6 +101,17 @@ int oracle_block_tokens(const oracle_block_cfg* cfg, const oracle_block_weights*
                         const void* x, int64_t n_tok, const int64_t* tokens,
                         const int32_t* idx, const double* w, double* y);
 
+/* Expert halves on given rows: h [R, d_ff] and out [R, d_in] in fp64. */
+int oracle_gate_up_rows(const oracle_block_cfg* cfg, const void* const* w1, const void* const* w3,
+                        int64_t R, const void* x_rows, const int32_t* expert, double* h);
+int oracle_down_rows(const oracle_block_cfg* cfg, const void* const* w2, int64_t R,
+                     const void* h_rows, const int32_t* expert, double* out);
+
+/* Weighted combine: y [N, width] fp64 from expert rows (dtype), inv_perm,
+ * fp32 routing weights and an optional residual (dtype). */
+int oracle_combine(int64_t N, int k, int64_t width, int dtype, const void* out_sorted,
+                   const int32_t* inv_perm, const float* w, const void* residual, double* y);
+
 #ifdef __cplusplus
 }
 #endif

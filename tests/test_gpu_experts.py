@@ -1,0 +1,115 @@
+"""moe_expert_gate_up, moe_expert_down and moe_combine against the oracle's
+per-row expert halves and combine, on ragged widths, empty experts, a hot
+expert, and row counts that select each tile height of the grouped GEMM."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from moe_testlib import (as_f64, assert_close_bf16, assert_close_f32, cfg_of, moe, needs_gpu,
+                         oracle_cfg, to_device, to_host, torch)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def segments(rng, N, E, k, hot=None, empty=()):
+    """Expert of each sorted row, from a random routing with k distinct experts per token."""
+    allowed = [e for e in range(E) if e not in empty]
+    rows = []
+    for _ in range(N):
+        if hot is not None:
+            rest = rng.choice([e for e in allowed if e != hot], k - 1, replace=False)
+            rows.append(np.concatenate([[hot], rest]))
+        else:
+            rows.append(rng.choice(allowed, k, replace=False))
+    idx = np.sort(np.array(rows, np.int32), axis=1)
+    counts, offsets, perm, inv = oracle.counts_perm(idx, E)
+    expert_of_row = np.repeat(np.arange(E, dtype=np.int32), counts)
+    return idx, offsets, perm, inv, expert_of_row
+
+
+CASES = [
+    # name, N, E, k, d_in, d_ff, act, hot, empty
+    ("rb4_silu", 200, 8, 4, 1000, 136, "silu", None, ()),
+    ("rb2_situ", 300, 32, 4, 200, 72, "situ", None, (3, 4)),
+    ("rb1_silu", 100, 64, 4, 512, 256, "silu", None, (0,)),
+    ("hot_expert", 257, 16, 3, 136, 64, "silu", 5, ()),
+    ("wide", 16, 16, 8, 7168, 2048, "silu", None, ()),
+    ("latent_shape_situ", 10, 16, 8, 3584, 3072, "situ", None, ()),
+]
+
+
+def _workload(N, E, k, d_in, d_ff, act, dtype):
+    return synth.Workload(name="experts", N=N, d=d_in, E=E, G=1, TG=1, k=k, d_ff=d_ff,
+                          route_scale=1.0, act=act, situ_beta=4.0 if act == "situ" else 1.0,
+                          situ_linear_beta=8.0 if act == "situ" else 0.0, dtype=dtype, seed=E)
+
+
+@pytest.mark.parametrize("name,N,E,k,d_in,d_ff,act,hot,empty", CASES)
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32])
+def test_gate_up_and_down(name, N, E, k, d_in, d_ff, act, hot, empty, dtype):
+    if dtype == synth.F32 and d_in > 1024:
+        pytest.skip("fp32 path is the tiny-workload path; wide shapes run in bf16")
+    print(f"experts parity: {name} dtype={dtype}", flush=True)
+    rng = np.random.default_rng(len(name))
+    m = moe()
+    w = _workload(N, E, k, d_in, d_ff, act, dtype)
+    cfg = cfg_of(w)
+    bf16 = dtype == synth.BF16
+    idx, offsets, perm, inv, erow = segments(rng, N, E, k, hot, empty)
+    S = N * k
+    x = synth.fill_normal_host(S * d_in, 0, 7, 1, 1.0, dtype).reshape(S, d_in)
+    W = {n: synth.host_tensor(w, n) for n in ("w1", "w3", "w2")}
+    dW = {n: to_device(a, bf16) for n, a in W.items()}
+    doffs = torch.from_numpy(offsets).cuda()
+    h = torch.empty((S, d_ff), dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
+    m.moe_expert_gate_up(cfg, N, to_device(x, bf16), doffs, dW["w1"], dW["w3"], h,
+                         m.workspace(cfg, N, m.CALL_GATE_UP))
+    torch.cuda.synchronize()
+    ocfg = oracle_cfg(w)
+    h_ref = oracle.gate_up_rows(ocfg, W["w1"], W["w3"], x, erow)
+    if bf16:
+        assert_close_bf16(as_f64(to_host(h)), h_ref, "gate_up")
+    else:
+        assert_close_f32(to_host(h), h_ref, "gate_up")
+
+    # down on an independent input of the same shape
+    hin = synth.fill_normal_host(S * d_ff, 0, 8, 1, 0.5, dtype).reshape(S, d_ff)
+    out = torch.empty((S, d_in), dtype=h.dtype, device="cuda")
+    m.moe_expert_down(cfg, N, to_device(hin, bf16), doffs, dW["w2"], out,
+                      m.workspace(cfg, N, m.CALL_DOWN))
+    torch.cuda.synchronize()
+    o_ref = oracle.down_rows(ocfg, W["w2"], hin, erow)
+    if bf16:
+        assert_close_bf16(as_f64(to_host(out)), o_ref, "down")
+    else:
+        assert_close_f32(to_host(out), o_ref, "down")
+
+
+@pytest.mark.parametrize("N,k,width,residual", [(1, 1, 8, False), (100, 4, 200, True),
+                                                (513, 8, 7168, True), (64, 16, 3584, False)])
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32])
+def test_combine(N, k, width, residual, dtype):
+    rng = np.random.default_rng(N + k)
+    m = moe()
+    E = max(2 * k, 16)
+    w = synth.Workload(name="comb", N=N, d=width, E=E, G=1, TG=1, k=k, d_ff=8, route_scale=1.0,
+                       dtype=dtype)
+    cfg = cfg_of(w)
+    bf16 = dtype == synth.BF16
+    idx, offsets, perm, inv, _ = segments(rng, N, E, k)
+    S = N * k
+    outs = synth.fill_normal_host(S * width, 0, 9, 1, 1.0, dtype).reshape(S, width)
+    wts = rng.uniform(0.05, 1.0, (N, k)).astype(np.float32)
+    res = synth.fill_normal_host(N * width, 0, 10, 1, 1.0, dtype).reshape(N, width) if residual else None
+    y = torch.empty((N, width), dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
+    m.moe_combine(cfg, N, to_device(outs, bf16), torch.from_numpy(inv).cuda(),
+                  torch.from_numpy(wts).cuda(), to_device(res, bf16) if residual else None, y)
+    torch.cuda.synchronize()
+    y_ref = oracle.combine(outs, inv, wts, res)
+    got = as_f64(to_host(y))
+    if bf16:
+        # one rounding of the fp32 sum: within half an ulp of bf16 plus fp32 error
+        assert np.all(np.abs(got - y_ref) <= np.abs(y_ref) * 2.0 ** -8 + 1e-6)
+    else:
+        np.testing.assert_allclose(got, y_ref, rtol=1e-5, atol=1e-6)
