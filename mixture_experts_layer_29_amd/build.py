@@ -11,7 +11,7 @@ CSRC = os.path.join(_HERE, "csrc")
 BUILD = os.path.join(_HERE, "_build")
 LIB = os.path.join(_HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_f32.hip", "combine.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(os.path.dirname(_HERE), "include")]

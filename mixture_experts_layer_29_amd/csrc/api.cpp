@@ -293,7 +293,8 @@ moe_status run_route(const moe_config* c, int64_t N, const void* hidden, const f
     a.C = logits;
     a.ldc = E;
     a.c_rows = N;
-    CHECK_HIP(moe::launch_gemm_bf16(a, moe::EPI_STORE_F32, moe::A_REPEAT, dense_rb(N), 0, s));
+    // one n-tile spans 256 experts, so short m-tiles are what fills the GPU
+    CHECK_HIP(moe::launch_gemm_bf16(a, moe::EPI_STORE_F32, moe::A_REPEAT, N > 4096 ? 2 : 1, 0, s));
   } else {
     CHECK_HIP(dense_gemm(c, hidden, N, c->d, w_router, nullptr, E, logits, moe::EPI_STORE, nullptr, s));
   }

@@ -1,0 +1,72 @@
+// gemm_common.h - pieces shared by the bf16 MFMA and the fp32 GEMM kernels:
+// tile location, the XCD-aware work-group order, and the expert activations.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+namespace gemm {
+
+// Work-groups are dispatched to the 8 XCDs round-robin (id % 8).  Logical tile
+// L = (id % 8) * (grid / 8) + id / 8 gives each XCD a contiguous run of tiles.
+// The grid is a multiple of 8.
+__device__ __forceinline__ int64_t remap_xcd(int64_t bid, int64_t nwg) {
+  const int64_t per = nwg >> 3;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+// Expert activations (Kimi K3 "Gate features" page: expert and situ excerpts):
+// SiLU: silu(g) * u;  SiTU: beta*tanh(g/beta)*sigmoid(g) * (lb*tanh(u/lb) or u),
+// all in fp32.
+__device__ __forceinline__ float act_pair(int act, float g, float u, float beta, float lbeta) {
+  if (act == ACT_SILU) return g / (1.0f + expf(-g)) * u;
+  const float a = beta * tanhf(g / beta) * (1.0f / (1.0f + expf(-g)));
+  const float up = lbeta > 0.0f ? lbeta * tanhf(u / lbeta) : u;
+  return a * up;
+}
+
+struct TileLoc {
+  int64_t seg;
+  int64_t row0;  // first row of the tile in the concatenated row space
+  int rows;      // rows of the tile that exist (1 .. BM)
+  int64_t j;     // n-tile
+};
+
+// Logical tile L -> (segment, m-tile, n-tile).  Grouped: tiles are numbered
+// segment by segment; inside a segment n-tile-major with the m-tiles adjacent,
+// so the m-tiles that share one weight tile run side by side.  Dense: the same
+// with one segment.  False when L is past the last tile.
+template <int BM>
+__device__ __forceinline__ bool locate(const GemmArgs& a, int64_t L, int64_t n_tiles_n,
+                                       TileLoc& t) {
+  if (a.seg_off) {
+    const int64_t u = L / n_tiles_n;  // m-tile index
+    if (u >= a.tile_cap) return false;
+    const int32_t seg = a.tile_seg[u];
+    if (seg < 0) return false;
+    const int64_t MB = a.mt_off[seg];
+    const int64_t mt = a.mt_off[seg + 1] - MB;
+    const int64_t r = L - MB * n_tiles_n;
+    const int64_t j = r / mt, i = r - j * mt;
+    const int64_t s0 = a.seg_off[seg];
+    const int64_t s1 = min((int64_t)a.seg_off[seg + 1], a.c_rows);
+    t.seg = seg;
+    t.row0 = s0 + i * BM;
+    t.rows = (int)min((int64_t)BM, s1 - t.row0);
+    t.j = j;
+    return t.row0 >= 0 && t.rows > 0;
+  }
+  const int64_t mt = (a.dense_rows + BM - 1) / BM;
+  if (L >= mt * n_tiles_n) return false;
+  const int64_t j = L / mt, i = L - j * mt;
+  t.seg = 0;
+  t.row0 = i * BM;
+  t.rows = (int)min((int64_t)BM, a.dense_rows - t.row0);
+  t.j = j;
+  return true;
+}
+
+inline int64_t round8(int64_t n) { return (n + 7) & ~(int64_t)7; }
+
+}  // namespace gemm
+}  // namespace moe
