@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--workload", default="dsv3_prefill")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calibrate-copy-mb", type=int, default=0,
+                   help="first run one plain device copy of this many MiB (a known-size "
+                        "reference for hardware byte counters)")
     return p.parse_args()
 
 
@@ -163,6 +166,14 @@ def main():
     ws = m.workspace(cfg, w.N, m.CALL_BLOCK)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
+    if args.calibrate_copy_mb:
+        n = args.calibrate_copy_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         m.moe_block_forward(cfg, w.N, weights, dev["hidden"], y, ws, tokens_per_expert_out=counts)

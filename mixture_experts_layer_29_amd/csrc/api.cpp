@@ -134,14 +134,25 @@ struct Carver {
   }
 };
 
+// Height (in 32-row blocks) of the routed grouped-GEMM tiles.  A tile streams
+// its weight columns once for all of its rows, so the tile should hold a whole
+// expert segment where it can (each extra m-tile of an expert re-streams the
+// expert's weights); tiles shorter than their maximum issue only the MFMAs of
+// their rows.  Taller tiles need more accumulator registers (one wave per SIMD
+// from 4 blocks up), so short segments (decode) use short tiles.  Widths that
+// are not multiples of 64 take the clamped K-tail path, which runs 1-block tiles.
 int choose_rb(const moe_config* c, int64_t N) {
+  const int64_t d_in = c->d_latent > 0 ? c->d_latent : c->d;
+  if (d_in % 64 || c->d_ff % 64) return 1;
   const double avg = (double)N * c->top_k / (double)c->n_experts;
-  if (avg >= 80.0) return 4;
-  if (avg >= 24.0) return 2;
+  if (avg >= 64.0) return 8;
+  if (avg >= 24.0) return 4;
+  if (avg >= 12.0) return 2;
   return 1;
 }
 
-int dense_rb(int64_t rows) {
+int dense_rb(int64_t rows, int64_t K) {
+  if (K % 64) return 1;
   if (rows >= 2048) return 4;
   if (rows >= 512) return 2;
   return 1;
@@ -239,7 +250,7 @@ hipError_t dense_gemm(const moe_config* c, const void* A, int64_t rows, int64_t 
   a.act = c->act;
   a.beta = c->situ_beta > 0.0f ? c->situ_beta : 1.0f;
   a.lbeta = c->situ_linear_beta;
-  if (is_bf16(c)) return moe::launch_gemm_bf16(a, epi, moe::A_DIRECT, dense_rb(rows), 0, s);
+  if (is_bf16(c)) return moe::launch_gemm_bf16(a, epi, moe::A_DIRECT, dense_rb(rows, K), 0, s);
   return moe::launch_gemm_f32(a, epi, moe::A_DIRECT, 0, s);
 }
 

@@ -6,34 +6,40 @@
 // row-major, weights W in nn.Linear layout [cols, K] (the expert excerpt of the
 // Kimi K3 "Gate features" page: w1, w3 [d_ff, d_in], w2 [d_in, d_ff], no bias).
 //
-// Design for CDNA4, where at every MoE size of interest the expert weights, not
-// the flops, set the time (each weight byte feeds only the T_e rows routed to
-// its expert):
-//  - a work-group (4 waves) owns one (segment, n-tile, m-tile); each wave owns
-//    two 32-column blocks of the output and streams its weight rows straight
-//    from HBM into registers in the operand layout of
-//    v_mfma_f32_32x32x16_bf16, D blocks of 64 k ahead (no LDS round trip for
-//    weights: each weight element feeds exactly one wave);
-//  - the activation tile (up to RB x 32 rows x 64 k) is shared by the 4 waves
-//    through double-buffered LDS, loaded into registers two blocks ahead; in
-//    gather mode its rows are read through the dispatch permutation, so no
-//    expert-sorted copy of the input is ever written;
-//  - the steady-state loop has no branches and no data-dependent waits: every
-//    load is unconditional, the loads of an iteration are issued in the order
-//    A(kb+2), B(kb+D) so that the in-order vmcnt wait before an LDS store never
-//    waits on weight loads issued after it; the last blocks are peeled;
-//  - the number of 32-row blocks that hold rows is a template parameter, so a
-//    tile with few rows issues only the MFMAs it needs (decode tiles of a few
-//    rows and prefill tiles of hundreds run the same kernel);
+// Design for CDNA4.  At the MoE sizes of interest the expert weights set the
+// time, and each weight byte feeds only the T_e rows routed to its expert, so
+// the kernel is built to stream every expert's weights once at close to full
+// HBM bandwidth with the MFMAs for its rows running underneath:
+//  - a work-group (4 waves) owns one (segment, n-tile, m-tile); tiles are up to
+//    RB x 32 rows high so that a whole expert segment usually fits one tile
+//    (every extra m-tile of an expert would stream its weights again);
+//  - each wave owns two 32-column blocks of the output (the gate and the up
+//    block of the same columns for the gate/up product);
+//  - both operands are copied from HBM straight into LDS by the load units
+//    (global_load_lds_dwordx4: 16 bytes per lane, 8 lanes per 128-byte line of
+//    a row, no registers held while in flight), weights SB-1 blocks of 64 k
+//    ahead in an SB-stage ring, activations one block ahead; under full load
+//    HBM latency is several microseconds, so the bytes in flight per CU (about
+//    (SB-1) x 32 KB) are what sets the achievable bandwidth;
+//  - waits are explicit (vmcnt counts of the loads issued since) followed by a
+//    plain work-group barrier, so loads for later blocks stay in flight;
+//  - LDS tiles are unpadded 128-byte rows whose 16-byte chunks are
+//    XOR-swizzled by bits 1..3 of the row (each lane fetches the chunk that
+//    belongs at its fixed LDS slot): the MFMA-layout reads touch all 64 banks
+//    once per 16 lanes;
+//  - fragments are read in the operand layout of v_mfma_f32_32x32x16_bf16; the
+//    number of 32-row blocks that hold rows is a template parameter, so a tile
+//    with few rows issues only the MFMAs (and activation loads) it needs;
+//  - in gather mode activation rows are read through the dispatch
+//    permutation, so no expert-sorted copy of the input is ever written;
 //  - tiles are numbered segment-major, then n-tile, then m-tile, and mapped to
-//    work-group ids so that consecutive tiles land on the same XCD (weight and
-//    activation tiles shared under one L2);
+//    work-group ids so that consecutive tiles land on the same XCD;
 //  - the epilogue stages the fp32 accumulators through LDS, applies
 //    SiLU/SiTU-and-mul or the residual add in fp32, rounds once and writes
 //    16-byte row-contiguous chunks.
 // Inside a 64-wide K block the lanes visit K in an order of our choosing, the
-// same for both operands, which lets a lane read 64 contiguous bytes of its
-// weight row per block.
+// same for both operands (lane half h takes elements 32h .. 32h+31, eight per
+// MFMA step).
 #include "gemm_common.h"
 
 namespace moe {
@@ -41,91 +47,148 @@ namespace {
 
 using gemm::TileLoc;
 
+#define MOE_GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
+#define MOE_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kLdsA = 72;    // bf16 per LDS activation row: 64 + 8 pad (conflict-free b128 reads)
-constexpr int kLdsOut = 72;  // fp32 per LDS epilogue row: 64 + 8 pad
-constexpr int kLdsBytesOut = kWaves * 32 * kLdsOut * 4;
+constexpr int kRowBytes = 128;                      // one 64-element K block of a bf16 row
+constexpr int kBRows = 64;                          // weight rows per wave (two 32-column blocks)
+constexpr int kBWave = kBRows * kRowBytes;          // 8 KB
+constexpr int kBStage = kWaves * kBWave;            // 32 KB
+constexpr int kLdsOut = 72;                         // fp32 per LDS epilogue row: 64 + 8 pad
+constexpr int kEpiBytes = kWaves * 32 * kLdsOut * 4;
 
-template <int RB>
+template <int RB, int SB>
 struct Smem {
-  static constexpr int kA = 2 * RB * 32 * kLdsA * 2;
-  static constexpr int kBytes = kA > kLdsBytesOut ? kA : kLdsBytesOut;
+  static constexpr int kATile = RB * 32 * kRowBytes;
+  static constexpr int kA = 2 * kATile;  // activations: two stages
+  static constexpr int kB = SB * kBStage;
+  static constexpr int kBytes = (kA + kB) > kEpiBytes ? (kA + kB) : kEpiBytes;
 };
 
-template <int NR, int RB, int EPI, int AMODE, int D, bool KT>
+// Byte offset of 16-byte chunk `c` of row `r` in a swizzled 128-byte-row tile.
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * kRowBytes + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+// Compiler-level fence: no memory access moves across it (IR or scheduler).
+__device__ __forceinline__ void code_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt on the vector-memory counter only (lgkm and exp left free).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  code_fence();
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  code_fence();
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  code_fence();
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+  code_fence();
+}
+// Work-group barrier without the memory fence of __syncthreads (whose release
+// semantics would wait for every load in flight, including the prefetches).
+// LDS visibility is arranged by the explicit waits before it.
+__device__ __forceinline__ void wg_barrier() {
+  code_fence();
+  __builtin_amdgcn_s_barrier();
+  code_fence();
+}
+
+constexpr int lcm_c(int a, int b) {
+  int x = a, y = b;
+  while (y) {
+    const int t = x % y;
+    x = y;
+    y = t;
+  }
+  return a / x * b;
+}
+
+// NR: 32-row blocks holding rows; SB: weight stages (prefetch distance SB-1).
+template <int NR, int RB, int EPI, int AMODE, int SB, bool KT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, uint8_t* smem) {
+  static_assert(SB >= 3, "the wait counts assume weights at least two blocks ahead");
   constexpr int CPW = (EPI == EPI_GATE_UP) ? 32 : 64;  // output columns per wave
-  constexpr int U = (D % 2 == 0) ? D : 2 * D;          // unroll: ring slots stay static
-  bf16_t(*As)[RB * 32][kLdsA] = reinterpret_cast<bf16_t(*)[RB * 32][kLdsA]>(smem);
+  constexpr int U = lcm_c(2, SB);                      // unroll: stage indices stay static
+  constexpr int ATILE = Smem<RB, SB>::kATile;
+  uint8_t* const As = smem;                            // [2][RB*32 rows][128 B]
+  uint8_t* const Bs = smem + Smem<RB, SB>::kA;         // [SB][wave][64 rows][128 B]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int64_t K = a.K;
   const int64_t nkb = (K + 63) >> 6;
+  const int slot = lane & 7;  // LDS chunk slot this lane's load lands in
 
-  // ---- weight rows of this lane: column lane&31 of the wave's two blocks
+  // ---- weights: instruction i fills wave rows 8i..8i+7; rows 0..31 are block 0
+  // (columns cb0..), rows 32..63 block 1 (columns cb1..)
   const int64_t cb0 = t.j * (kWaves * CPW) + (int64_t)wave * CPW;
   const int64_t cb1 = (EPI == EPI_GATE_UP) ? cb0 : cb0 + 32;
-  const int64_t cl = lane & 31;
-  const int64_t c0 = min(cb0 + cl, a.n_cols - 1);
-  const int64_t c1 = min(cb1 + cl, a.n_cols - 1);
   const bf16_t* W0 = static_cast<const bf16_t*>(a.B0) + t.seg * a.b_seg_stride;
   const bf16_t* W1 =
       static_cast<const bf16_t*>(EPI == EPI_GATE_UP ? a.B1 : a.B0) + t.seg * a.b_seg_stride;
-  const int kq = (lane >> 5) * 32;  // this lane's 32-element half of each 64-block
-  const bf16_t* bp0 = W0 + c0 * K + kq;
-  const bf16_t* bp1 = W1 + c1 * K + kq;
-
-  // ---- activation rows this thread stages: NR chunks of 16 bytes
-  const int seg8 = tid & 7;
-  const bf16_t* ap[NR];
+  const bf16_t* brow[8];  // this lane's source (row, chunk) for each instruction
+  int bchunk[8];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const int row = (tid >> 3) + 32 * r;
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    bchunk[i] = slot ^ ((r >> 1) & 7);
+    // columns past the end reload the last column (their outputs are dropped)
+    const int64_t c = min((i < 4 ? cb0 : cb1) + 8 * (i & 3) + (lane >> 3), a.n_cols - 1);
+    brow[i] = (i < 4 ? W0 : W1) + c * K + bchunk[i] * 8;
+  }
+
+  // ---- activations: wave w fills tile rows 8(w*NR + i) .. +7 with instruction i
+  const bf16_t* ap[NR];
+  int achunk[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int row = 8 * (wave * NR + i) + (lane >> 3);
+    achunk[i] = slot ^ ((row >> 1) & 7);
     int64_t src = t.row0 + (row < t.rows ? row : 0);
     if (AMODE == A_GATHER) src = a.a_map[src] / a.a_div;
     src = src < 0 ? 0 : (src >= a.a_rows ? a.a_rows - 1 : src);
-    ap[r] = static_cast<const bf16_t*>(a.A) + src * a.lda + seg8 * 8;
+    ap[i] = static_cast<const bf16_t*>(a.A) + src * a.lda + achunk[i] * 8;
   }
   const int64_t a_per_blocks = AMODE == A_REPEAT ? (a.a_period >> 6) : 1;
 
-  auto a_col = [&](int64_t kb) -> int64_t {
-    int64_t col = (AMODE == A_REPEAT ? (kb % a_per_blocks) : kb) * 64;
-    if (AMODE == A_REPEAT) {
-      // columns past the valid width meet zero weights: any finite value will do
-      col = min(col, a.a_valid - 8 - seg8 * 8);
-    } else if (KT) {
-      col = min(col, K - 8 - seg8 * 8);
-    }
-    return col;
-  };
-  auto load_a = [&](int64_t kb, u32x4 (&areg)[NR]) {
-    const int64_t col = a_col(kb);
+  auto issue_a = [&](int64_t kb, int stage) {
+    const int64_t col = (AMODE == A_REPEAT ? (kb % a_per_blocks) : kb) * 64;
+    uint8_t* const dst = As + stage * ATILE + wave * NR * 1024;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) areg[r] = *reinterpret_cast<const u32x4*>(ap[r] + col);
-  };
-  auto store_a = [&](int buf, int64_t kb, const u32x4 (&areg)[NR]) {
-    bool live = true;
-    if (KT && AMODE != A_REPEAT) live = kb * 64 + seg8 * 8 < K;  // zero past the K tail
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int row = (tid >> 3) + 32 * r;
-      u32x4 v = areg[r];
-      if (KT && AMODE != A_REPEAT && !live) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&As[buf][row][seg8 * 8]) = v;
+    for (int i = 0; i < NR; ++i) {
+      int64_t c = col;
+      // past the valid width: A_REPEAT meets zero weights, the K tail is zeroed
+      // in LDS after the copy; either way the address stays inside the row
+      if (AMODE == A_REPEAT) c = min(c, a.a_valid - 8 - achunk[i] * 8);
+      else if (KT) c = min(c, K - 8 - achunk[i] * 8);
+      __builtin_amdgcn_global_load_lds(MOE_GPTR(ap[i] + c), MOE_LPTR(dst + i * 1024), 16, 0, 0);
     }
   };
-
-  u32x4 breg[D][2][4];
-  auto load_b = [&](int64_t kb, u32x4 (&b)[2][4]) {
+  auto issue_b = [&](int64_t kb, int stage) {
+    uint8_t* const dst = Bs + stage * kBStage + wave * kBWave;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      int64_t off = kb * 64 + s * 8;
-      if (KT) off = min(off, K - 8 - kq);  // stay inside the row; A is zero there
-      b[0][s] = *reinterpret_cast<const u32x4*>(bp0 + off);
-      b[1][s] = *reinterpret_cast<const u32x4*>(bp1 + off);
+    for (int i = 0; i < 8; ++i) {
+      int64_t off = kb * 64;
+      if (KT) off = min(off, K - 8 - bchunk[i] * 8);  // A is zero there
+      __builtin_amdgcn_global_load_lds(MOE_GPTR(brow[i] + off), MOE_LPTR(dst + i * 1024), 16, 0, 0);
     }
+  };
+  // K tail: zero this lane's activation chunks of the last block that lie past K
+  auto zero_a_tail = [&](int64_t kb, int stage) {
+    uint8_t* const dst = As + stage * ATILE + wave * NR * 1024;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      if (kb * 64 + achunk[i] * 8 >= K)
+        *reinterpret_cast<u32x4*>(dst + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
+    wait_lgkm0();
   };
 
   f32x16 acc[NR][2];
@@ -138,68 +201,73 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
     }
   }
 
-  auto compute = [&](int buf, const u32x4 (&b)[2][4]) {
-    // all of the block's activation fragments first, then the MFMAs
-    bf16x8 af[4][NR];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int rb = 0; rb < NR; ++rb) {
-        af[s][rb] = *reinterpret_cast<const bf16x8*>(
-            &As[buf][rb * 32 + (lane & 31)][(lane >> 5) * 32 + s * 8]);
-      }
-    }
-    // keep the scheduler from sinking each read next to its MFMA (which would
-    // expose the LDS latency once per MFMA pair)
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 b0 = __builtin_bit_cast(bf16x8, b[0][s]);
-      const bf16x8 b1 = __builtin_bit_cast(bf16x8, b[1][s]);
+  // One K block from LDS: 4 MFMA steps; in step s lane half h reads chunk
+  // 4h + s of its rows.  The next step's fragments are read before the current
+  // step's MFMAs (fences keep the reads from sinking next to their MFMAs).
+  const int rsel = lane & 31;
+  const int cbase = (lane >> 5) * 4;
+  auto compute = [&](int astage, int bstage) {
+    const uint8_t* const at = As + astage * ATILE;
+    const uint8_t* const bt = Bs + bstage * kBStage + wave * kBWave;
+    bf16x8 af[2][NR];
+    bf16x8 bf[2][2];
+    auto read_frags = [&](int s, bf16x8 (&fa)[NR], bf16x8 (&fb)[2]) {
+      const int c = cbase + s;
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb) {
-        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][rb], b0, acc[rb][0], 0, 0, 0);
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][rb], b1, acc[rb][1], 0, 0, 0);
+        fa[rb] = *reinterpret_cast<const bf16x8*>(at + swz(rb * 32 + rsel, c));
       }
+      fb[0] = *reinterpret_cast<const bf16x8*>(bt + swz(rsel, c));
+      fb[1] = *reinterpret_cast<const bf16x8*>(bt + swz(32 + rsel, c));
+    };
+    read_frags(0, af[0], bf[0]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) read_frags(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < NR; ++rb) {
+        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][rb], bf[s & 1][0], acc[rb][0], 0, 0, 0);
+        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][rb], bf[s & 1][1], acc[rb][1], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // ---- prologue
-  u32x4 areg[2][NR];
-  load_a(0, areg[0]);
-#pragma unroll
-  for (int q = 0; q < D; ++q) {
-    if (q < nkb) load_b(q, breg[q]);
+  // ---- pipeline.  Iteration m issues A(m+1) then B(m+SB-1), after the barrier
+  // that ends every wave's reads of the stages they overwrite.  At the top of
+  // iteration kb the loads younger than A(kb) are just B(kb+SB-2), 8 per wave
+  // (when it exists), and B(kb) is older than A(kb): waiting for at most 8
+  // outstanding loads leaves block kb complete.
+  for (int q = 0; q + 2 < SB; ++q) {
+    if (q < nkb) issue_b(q, q);
   }
-  if (nkb > 1) load_a(1, areg[1]);
-  store_a(0, 0, areg[0]);
-  __syncthreads();
+  issue_a(0, 0);
+  if (SB - 2 < nkb) issue_b(SB - 2, SB - 2);
 
-  // ---- steady state: every sub-iteration has kb + D < nkb (so kb + 2 < nkb too)
+  auto step = [&](int64_t kb, int q, bool steady) {
+    if (steady || kb + SB - 2 < nkb) {
+      wait_vm<8>();
+    } else {
+      wait_vm<0>();
+    }
+    if (KT && AMODE != A_REPEAT && kb == nkb - 1) zero_a_tail(kb, q & 1);
+    wg_barrier();
+    if (steady || kb + 1 < nkb) issue_a(kb + 1, (q + 1) & 1);
+    if (steady || kb + SB - 1 < nkb) issue_b(kb + SB - 1, (q + SB - 1) % SB);
+    compute(q & 1, q % SB);
+  };
   int64_t kb0 = 0;
-  for (; kb0 + (U - 1) + D < nkb; kb0 += U) {
+  for (; kb0 + (U - 1) + (SB - 1) < nkb; kb0 += U) {
 #pragma unroll
-    for (int q = 0; q < U; ++q) {
-      const int64_t kb = kb0 + q;
-      load_a(kb + 2, areg[q % 2]);
-      compute(q % 2, breg[q % D]);
-      load_b(kb + D, breg[q % D]);
-      store_a((q + 1) % 2, kb + 1, areg[(q + 1) % 2]);
-      __syncthreads();
-    }
+    for (int q = 0; q < U; ++q) step(kb0 + q, q, true);
   }
-  // ---- drain: fewer than U + D blocks remain
 #pragma unroll
-  for (int q = 0; q < U + D; ++q) {
-    const int64_t kb = kb0 + q;
-    if (kb < nkb) {
-      if (kb + 2 < nkb) load_a(kb + 2, areg[q % 2]);
-      compute(q % 2, breg[q % D]);
-      if (kb + D < nkb) load_b(kb + D, breg[q % D]);
-      if (kb + 1 < nkb) store_a((q + 1) % 2, kb + 1, areg[(q + 1) % 2]);
-      __syncthreads();
-    }
+  for (int q = 0; q < U + SB - 1; ++q) {
+    if (kb0 + q < nkb) step(kb0 + q, q, false);
   }
+  wait_vm<0>();
+  __syncthreads();
 
   // ---- epilogue: through LDS as fp32, 16-byte row-contiguous stores.
   // MFMA layout: lane holds column lane&31, rows 8*(r/4) + 4*(lane/32) + r%4.
@@ -284,56 +352,60 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
   }
 }
 
-// RB = 4 tiles hold 128 accumulators per lane: one wave per SIMD, all registers.
-template <int RB, int EPI, int AMODE, int D, bool KT>
+// Tiles of 4 or more row blocks hold 128+ accumulators per lane: one wave per SIMD.
+template <int RB, int EPI, int AMODE, int SB, bool KT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, RB >= 4 ? 1 : 2)))
 void moe_gemm_bf16(GemmArgs a, int64_t n_tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<RB>::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<RB, SB>::kBytes];
   TileLoc t;
   if (!gemm::locate<RB * 32>(a, gemm::remap_xcd(blockIdx.x, gridDim.x), n_tiles_n, t)) return;
   const int nrb = (t.rows + 31) >> 5;
-  if (nrb <= 1) {
-    gemm_tile<1, RB, EPI, AMODE, D, KT>(a, t, smem);
-  } else if (nrb == 2) {
-    if constexpr (RB >= 2) gemm_tile<2, RB, EPI, AMODE, D, KT>(a, t, smem);
-  } else if (nrb == 3) {
-    if constexpr (RB >= 3) gemm_tile<3, RB, EPI, AMODE, D, KT>(a, t, smem);
-  } else {
-    if constexpr (RB >= 4) gemm_tile<4, RB, EPI, AMODE, D, KT>(a, t, smem);
+  switch (nrb) {
+    case 1: gemm_tile<1, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
+    case 2: if constexpr (RB >= 2) gemm_tile<2, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
+    case 3: if constexpr (RB >= 3) gemm_tile<3, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
+    case 4: if constexpr (RB >= 4) gemm_tile<4, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
+    case 5: if constexpr (RB >= 5) gemm_tile<5, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
+    case 6: if constexpr (RB >= 6) gemm_tile<6, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
+    case 7: if constexpr (RB >= 7) gemm_tile<7, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
+    default: if constexpr (RB >= 8) gemm_tile<8, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
   }
 }
 
 template <int RB, int EPI, int AMODE, bool KT>
 hipError_t launch_rb(const GemmArgs& a, int64_t mt_cap, hipStream_t s) {
-  constexpr int D = (RB >= 4) ? 3 : 4;
+  // weight stages: as deep as the 160 KB of LDS allows next to the activations
+  constexpr int SB = (RB >= 8) ? 3 : 4;
   constexpr int CPW = (EPI == EPI_GATE_UP) ? 32 : 64;
   const int64_t n_tiles_n = (a.n_cols + kWaves * CPW - 1) / (kWaves * CPW);
   const int64_t mt = a.seg_off ? mt_cap : (a.dense_rows + RB * 32 - 1) / (RB * 32);
   const int64_t grid = gemm::round8(mt * n_tiles_n);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  moe_gemm_bf16<RB, EPI, AMODE, D, KT><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a, n_tiles_n);
+  moe_gemm_bf16<RB, EPI, AMODE, SB, KT><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a, n_tiles_n);
   return hipGetLastError();
 }
 
+// Tile heights: rb in {1, 2, 4, 8} row blocks of 32.  A K that is not a
+// multiple of 64 (odd shapes only) runs the clamped variant, with rb = 1.
 template <int EPI, int AMODE>
 hipError_t launch_any(const GemmArgs& a, int rb, int64_t mt_cap, hipStream_t s) {
   const bool kt = (a.K % 64) != 0 && AMODE != A_REPEAT;
   if (kt) {
     if constexpr (AMODE != A_REPEAT) {
-      switch (rb) {
-        case 1: return launch_rb<1, EPI, AMODE, true>(a, mt_cap, s);
-        case 2: return launch_rb<2, EPI, AMODE, true>(a, mt_cap, s);
-        case 4: return launch_rb<4, EPI, AMODE, true>(a, mt_cap, s);
-        default: return hipErrorInvalidValue;
-      }
+      if (rb == 1) return launch_rb<1, EPI, AMODE, true>(a, mt_cap, s);
     }
     return hipErrorInvalidValue;
   }
   switch (rb) {
     case 1: return launch_rb<1, EPI, AMODE, false>(a, mt_cap, s);
     case 2: return launch_rb<2, EPI, AMODE, false>(a, mt_cap, s);
-    case 4: return launch_rb<4, EPI, AMODE, false>(a, mt_cap, s);
+    case 4:
+      if constexpr (AMODE != A_REPEAT) return launch_rb<4, EPI, AMODE, false>(a, mt_cap, s);
+      return hipErrorInvalidValue;
+    case 8:
+      if constexpr (AMODE != A_REPEAT) return launch_rb<8, EPI, AMODE, false>(a, mt_cap, s);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
