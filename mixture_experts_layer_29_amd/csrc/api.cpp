@@ -139,8 +139,9 @@ struct Carver {
 // expert segment where it can (each extra m-tile of an expert re-streams the
 // expert's weights); tiles shorter than their maximum issue only the MFMAs of
 // their rows.  Taller tiles need more accumulator registers (one wave per SIMD
-// from 4 blocks up), so short segments (decode) use short tiles.  Widths that
-// are not multiples of 64 take the clamped K-tail path, which runs 1-block tiles.
+// and a larger activation stage in LDS), so short segments (decode) use short
+// tiles.  Widths that are not multiples of 64 take the clamped K-tail path,
+// which runs 1-block tiles.
 int choose_rb(const moe_config* c, int64_t N) {
   const int64_t d_in = c->d_latent > 0 ? c->d_latent : c->d;
   if (d_in % 64 || c->d_ff % 64) return 1;

@@ -16,20 +16,27 @@
 //  - each wave owns two 32-column blocks of the output (the gate and the up
 //    block of the same columns for the gate/up product);
 //  - both operands are copied from HBM straight into LDS by the load units
-//    (global_load_lds_dwordx4: 16 bytes per lane, 8 lanes per 128-byte line of
-//    a row, no registers held while in flight), weights SB-1 blocks of 64 k
-//    ahead in an SB-stage ring, activations one block ahead; under full load
-//    HBM latency is several microseconds, so the bytes in flight per CU (about
-//    (SB-1) x 32 KB) are what sets the achievable bandwidth;
-//  - waits are explicit (vmcnt counts of the loads issued since) followed by a
-//    plain work-group barrier, so loads for later blocks stay in flight;
+//    (global_load_lds_dwordx4: 16 bytes per lane, 8 lanes per 128-byte piece
+//    of a row, no registers held while in flight).  The weights stream as
+//    sub-blocks of one 32-column block x 64 k per wave (16 KB per work-group),
+//    SB-1 sub-blocks ahead in an SB-stage ring; the activations of a 64-k block
+//    serve its two column sub-blocks and are loaded one block ahead.  Under
+//    full load HBM latency is several microseconds, so the bytes in flight per
+//    CU ((SB-1) x 16 KB, 80-128 KB) set the achievable bandwidth, and each
+//    visit of a weight row reads a whole 128-byte piece (shorter pieces cost
+//    DRAM efficiency);
+//  - waits are explicit vmcnt counts followed by a plain work-group barrier, so
+//    loads for later sub-blocks stay in flight.  Every sub-iteration issues the
+//    same loads (past either end of K the last block is fetched again into the
+//    stage that is free), so the counts are compile-time constants;
 //  - LDS tiles are unpadded 128-byte rows whose 16-byte chunks are
 //    XOR-swizzled by bits 1..3 of the row (each lane fetches the chunk that
 //    belongs at its fixed LDS slot): the MFMA-layout reads touch all 64 banks
 //    once per 16 lanes;
-//  - fragments are read in the operand layout of v_mfma_f32_32x32x16_bf16; the
-//    number of 32-row blocks that hold rows is a template parameter, so a tile
-//    with few rows issues only the MFMAs (and activation loads) it needs;
+//  - fragments are read in the operand layout of v_mfma_f32_32x32x16_bf16, the
+//    reads for the next MFMA step interleaved with the current step's MFMAs;
+//    the number of 32-row blocks that hold rows is a template parameter, so a
+//    tile with few rows issues only the MFMAs (and activation loads) it needs;
 //  - in gather mode activation rows are read through the dispatch
 //    permutation, so no expert-sorted copy of the input is ever written;
 //  - tiles are numbered segment-major, then n-tile, then m-tile, and mapped to
@@ -40,6 +47,8 @@
 // Inside a 64-wide K block the lanes visit K in an order of our choosing, the
 // same for both operands (lane half h takes elements 32h .. 32h+31, eight per
 // MFMA step).
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace moe {
@@ -53,18 +62,25 @@ using gemm::TileLoc;
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kRowBytes = 128;                      // one 64-element K block of a bf16 row
-constexpr int kBRows = 64;                          // weight rows per wave (two 32-column blocks)
-constexpr int kBWave = kBRows * kRowBytes;          // 8 KB
-constexpr int kBStage = kWaves * kBWave;            // 32 KB
+constexpr int kBRows = 32;                          // weight rows per wave per sub-block
+constexpr int kBLoads = kBRows / 8;                 // loads per wave per sub-block: 4
+constexpr int kBWave = kBRows * kRowBytes;          // 4 KB
+constexpr int kBStage = kWaves * kBWave;            // 16 KB
+constexpr int kLdsMax = 160 * 1024;                 // LDS of one CU
 constexpr int kLdsOut = 72;                         // fp32 per LDS epilogue row: 64 + 8 pad
 constexpr int kEpiBytes = kWaves * 32 * kLdsOut * 4;
 
-template <int RB, int SB>
+// LDS plan of an RB-block tile: two activation stages, then as many weight
+// stages as fit (at most 9).
+template <int RB>
 struct Smem {
   static constexpr int kATile = RB * 32 * kRowBytes;
-  static constexpr int kA = 2 * kATile;  // activations: two stages
-  static constexpr int kB = SB * kBStage;
+  static constexpr int kA = 2 * kATile;
+  static constexpr int kFit = (kLdsMax - kA) / kBStage;
+  static constexpr int kSB = kFit > 9 ? 9 : kFit;
+  static constexpr int kB = kSB * kBStage;
   static constexpr int kBytes = (kA + kB) > kEpiBytes ? (kA + kB) : kEpiBytes;
+  static_assert(kBytes <= kLdsMax, "LDS plan exceeds one CU");
 };
 
 // Byte offset of 16-byte chunk `c` of row `r` in a swizzled 128-byte-row tile.
@@ -100,51 +116,44 @@ __device__ __forceinline__ void wg_barrier() {
   code_fence();
 }
 
-constexpr int lcm_c(int a, int b) {
-  int x = a, y = b;
-  while (y) {
-    const int t = x % y;
-    x = y;
-    y = t;
-  }
-  return a / x * b;
-}
-
-// NR: 32-row blocks holding rows; SB: weight stages (prefetch distance SB-1).
-template <int NR, int RB, int EPI, int AMODE, int SB, bool KT>
+// NR: 32-row blocks holding rows.  The weight ring has SB = Smem<RB>::kSB
+// stages of one column sub-block each.
+template <int NR, int RB, int EPI, int AMODE, bool KT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, uint8_t* smem) {
-  static_assert(SB >= 3, "the wait counts assume weights at least two blocks ahead");
+  constexpr int SB = Smem<RB>::kSB;
+  static_assert(SB >= 4, "the wait counts assume weights at least three sub-blocks ahead");
   constexpr int CPW = (EPI == EPI_GATE_UP) ? 32 : 64;  // output columns per wave
-  constexpr int U = lcm_c(2, SB);                      // unroll: stage indices stay static
-  constexpr int ATILE = Smem<RB, SB>::kATile;
+  constexpr int ATILE = Smem<RB>::kATile;
   uint8_t* const As = smem;                            // [2][RB*32 rows][128 B]
-  uint8_t* const Bs = smem + Smem<RB, SB>::kA;         // [SB][wave][64 rows][128 B]
+  uint8_t* const Bs = smem + Smem<RB>::kA;             // [SB][wave][32 rows][128 B]
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t K = a.K;
   const int64_t nkb = (K + 63) >> 6;
   const int slot = lane & 7;  // LDS chunk slot this lane's load lands in
 
-  // ---- weights: instruction i fills wave rows 8i..8i+7; rows 0..31 are block 0
-  // (columns cb0..), rows 32..63 block 1 (columns cb1..)
+  // ---- weights: sub-block (kb, c) holds the 32 rows of column block c of the
+  // wave (c = 0: columns cb0.., c = 1: columns cb1..); load i fills rows 8i..8i+7
   const int64_t cb0 = t.j * (kWaves * CPW) + (int64_t)wave * CPW;
   const int64_t cb1 = (EPI == EPI_GATE_UP) ? cb0 : cb0 + 32;
   const bf16_t* W0 = static_cast<const bf16_t*>(a.B0) + t.seg * a.b_seg_stride;
   const bf16_t* W1 =
       static_cast<const bf16_t*>(EPI == EPI_GATE_UP ? a.B1 : a.B0) + t.seg * a.b_seg_stride;
-  const bf16_t* brow[8];  // this lane's source (row, chunk) for each instruction
-  int bchunk[8];
+  const bf16_t* brow[2][kBLoads];  // this lane's source (row, chunk) per column block and load
+  int bchunk[kBLoads];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kBLoads; ++i) {
     const int r = 8 * i + (lane >> 3);
     bchunk[i] = slot ^ ((r >> 1) & 7);
     // columns past the end reload the last column (their outputs are dropped)
-    const int64_t c = min((i < 4 ? cb0 : cb1) + 8 * (i & 3) + (lane >> 3), a.n_cols - 1);
-    brow[i] = (i < 4 ? W0 : W1) + c * K + bchunk[i] * 8;
+    const int64_t c0 = min(cb0 + r, a.n_cols - 1);
+    const int64_t c1 = min(cb1 + r, a.n_cols - 1);
+    brow[0][i] = W0 + c0 * K + bchunk[i] * 8;
+    brow[1][i] = W1 + c1 * K + bchunk[i] * 8;
   }
 
-  // ---- activations: wave w fills tile rows 8(w*NR + i) .. +7 with instruction i
+  // ---- activations: wave w fills tile rows 8(w*NR + i) .. +7 with load i
   const bf16_t* ap[NR];
   int achunk[NR];
 #pragma unroll
@@ -158,7 +167,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
   }
   const int64_t a_per_blocks = AMODE == A_REPEAT ? (a.a_period >> 6) : 1;
 
+  // block indices are clamped to [0, nkb): a load past either end fetches a
+  // real block again, into a stage that nobody reads before it is refilled
   auto issue_a = [&](int64_t kb, int stage) {
+    kb = kb < 0 ? 0 : (kb >= nkb ? nkb - 1 : kb);
     const int64_t col = (AMODE == A_REPEAT ? (kb % a_per_blocks) : kb) * 64;
     uint8_t* const dst = As + stage * ATILE + wave * NR * 1024;
 #pragma unroll
@@ -171,13 +183,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
       __builtin_amdgcn_global_load_lds(MOE_GPTR(ap[i] + c), MOE_LPTR(dst + i * 1024), 16, 0, 0);
     }
   };
-  auto issue_b = [&](int64_t kb, int stage) {
+  auto issue_b = [&](int64_t kb, int cblk, int stage) {
+    kb = kb >= nkb ? nkb - 1 : kb;
     uint8_t* const dst = Bs + stage * kBStage + wave * kBWave;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kBLoads; ++i) {
       int64_t off = kb * 64;
       if (KT) off = min(off, K - 8 - bchunk[i] * 8);  // A is zero there
-      __builtin_amdgcn_global_load_lds(MOE_GPTR(brow[i] + off), MOE_LPTR(dst + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(MOE_GPTR(brow[cblk][i] + off), MOE_LPTR(dst + i * 1024), 16,
+                                       0, 0);
     }
   };
   // K tail: zero this lane's activation chunks of the last block that lie past K
@@ -201,70 +215,89 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
     }
   }
 
-  // One K block from LDS: 4 MFMA steps; in step s lane half h reads chunk
-  // 4h + s of its rows.  The next step's fragments are read before the current
-  // step's MFMAs (fences keep the reads from sinking next to their MFMAs).
+  // One column sub-block from LDS: 4 MFMA steps; in step s lane half h reads
+  // chunk 4h + s of its rows.  Step s+1's fragments are read between step s's
+  // MFMAs (a wave issues an MFMA only every few dozen cycles).
   const int rsel = lane & 31;
   const int cbase = (lane >> 5) * 4;
-  auto compute = [&](int astage, int bstage) {
-    const uint8_t* const at = As + astage * ATILE;
-    const uint8_t* const bt = Bs + bstage * kBStage + wave * kBWave;
+  auto compute = [&](auto cblk_tag, const uint8_t* at, const uint8_t* bt) {
+    constexpr int C = decltype(cblk_tag)::value;
     bf16x8 af[2][NR];
-    bf16x8 bf[2][2];
-    auto read_frags = [&](int s, bf16x8 (&fa)[NR], bf16x8 (&fb)[2]) {
+    bf16x8 bf[2];
+    auto read_frags = [&](int s, bf16x8 (&fa)[NR], bf16x8& fb) {
       const int c = cbase + s;
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb) {
         fa[rb] = *reinterpret_cast<const bf16x8*>(at + swz(rb * 32 + rsel, c));
       }
-      fb[0] = *reinterpret_cast<const bf16x8*>(bt + swz(rsel, c));
-      fb[1] = *reinterpret_cast<const bf16x8*>(bt + swz(32 + rsel, c));
+      fb = *reinterpret_cast<const bf16x8*>(bt + swz(rsel, c));
     };
     read_frags(0, af[0], bf[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s < 3) read_frags(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb) {
-        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][rb], bf[s & 1][0], acc[rb][0], 0, 0, 0);
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][rb], bf[s & 1][1], acc[rb][1], 0, 0, 0);
+        acc[rb][C] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][rb], bf[s & 1], acc[rb][C], 0, 0, 0);
+      }
+      if (s < 3) {
+        // MFMA, read, MFMA, read, ...: the reads hide under the MFMAs
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // ---- pipeline.  Iteration m issues A(m+1) then B(m+SB-1), after the barrier
-  // that ends every wave's reads of the stages they overwrite.  At the top of
-  // iteration kb the loads younger than A(kb) are just B(kb+SB-2), 8 per wave
-  // (when it exists), and B(kb) is older than A(kb): waiting for at most 8
-  // outstanding loads leaves block kb complete.
-  for (int q = 0; q + 2 < SB; ++q) {
-    if (q < nkb) issue_b(q, q);
+  // ---- pipeline over sub-iterations u = 2 kb + c.  Sub-iteration u (after
+  // its wait and barrier) issues, for even u only, A(kb + 1) into A stage
+  // (kb+1)&1, then sub-block u + SB - 1 into stage (u - 1) % SB: both stages
+  // were last read before the barrier.  The same happens for u = 1-SB .. -1
+  // before the loop (the prologue; A blocks below 0 fetch A(0) again).
+  //  - even u needs A(kb) (issued at u-2) and sub-block u (issued at
+  //    u-SB+1 <= u-3, hence older): the loads younger than A(kb) are the
+  //    weight loads of u-2 and u-1, so at most 2 kBLoads may stay outstanding;
+  //  - odd u needs sub-block u: younger are the loads of u-SB+2 .. u-1, kBLoads
+  //    each plus NR at each of their ceil((SB-2)/2) even sub-iterations.
+  constexpr int kWaitEven = 2 * kBLoads;
+  constexpr int kWaitOdd = kBLoads * (SB - 2) + NR * ((SB - 1) / 2);
+  static_assert(kWaitOdd < 64, "vmcnt range");
+#pragma unroll
+  for (int q = 0; q < SB - 1; ++q) {
+    // u = q - (SB-1); A(u/2 + 1) <= A(0), all into stage 0 (same bytes)
+    if (((q + SB - 1) & 1) == 0) issue_a(0, 0);
+    issue_b(q >> 1, q & 1, q);  // sub-block u + SB - 1 = q
   }
-  issue_a(0, 0);
-  if (SB - 2 < nkb) issue_b(SB - 2, SB - 2);
 
-  auto step = [&](int64_t kb, int q, bool steady) {
-    if (steady || kb + SB - 2 < nkb) {
-      wait_vm<8>();
-    } else {
-      wait_vm<0>();
-    }
-    if (KT && AMODE != A_REPEAT && kb == nkb - 1) zero_a_tail(kb, q & 1);
+  int sb = 0;  // stage of the sub-block being consumed
+  const uint8_t* const bt0 = Bs + wave * kBWave;
+  for (int64_t kb = 0; kb < nkb; ++kb) {
+    const int sa = (int)(kb & 1);
+    // c = 0
+    wait_vm<kWaitEven>();
+    if (KT && AMODE != A_REPEAT && kb == nkb - 1) zero_a_tail(kb, sa);
     wg_barrier();
-    if (steady || kb + 1 < nkb) issue_a(kb + 1, (q + 1) & 1);
-    if (steady || kb + SB - 1 < nkb) issue_b(kb + SB - 1, (q + SB - 1) % SB);
-    compute(q & 1, q % SB);
-  };
-  int64_t kb0 = 0;
-  for (; kb0 + (U - 1) + (SB - 1) < nkb; kb0 += U) {
-#pragma unroll
-    for (int q = 0; q < U; ++q) step(kb0 + q, q, true);
-  }
-#pragma unroll
-  for (int q = 0; q < U + SB - 1; ++q) {
-    if (kb0 + q < nkb) step(kb0 + q, q, false);
+    issue_a(kb + 1, sa ^ 1);
+    {
+      const int64_t ub = 2 * kb + SB - 1;
+      issue_b(ub >> 1, (SB - 1) & 1, sb == 0 ? SB - 1 : sb - 1);
+    }
+    compute(std::integral_constant<int, 0>{}, As + sa * ATILE, bt0 + sb * kBStage);
+    sb = (sb + 1 == SB) ? 0 : sb + 1;
+    // c = 1
+    wait_vm<kWaitOdd>();
+    wg_barrier();
+    {
+      const int64_t ub = 2 * kb + SB;
+      issue_b(ub >> 1, SB & 1, sb == 0 ? SB - 1 : sb - 1);
+    }
+    compute(std::integral_constant<int, 1>{}, As + sa * ATILE, bt0 + sb * kBStage);
+    sb = (sb + 1 == SB) ? 0 : sb + 1;
   }
   wait_vm<0>();
   __syncthreads();
@@ -352,37 +385,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
   }
 }
 
-// Tiles of 4 or more row blocks hold 128+ accumulators per lane: one wave per SIMD.
-template <int RB, int EPI, int AMODE, int SB, bool KT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, RB >= 4 ? 1 : 2)))
+// The LDS plan fills a CU, so one work-group (one wave per SIMD) runs per CU
+// and each wave may use the whole register file.
+template <int RB, int EPI, int AMODE, bool KT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void moe_gemm_bf16(GemmArgs a, int64_t n_tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<RB, SB>::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<RB>::kBytes];
   TileLoc t;
   if (!gemm::locate<RB * 32>(a, gemm::remap_xcd(blockIdx.x, gridDim.x), n_tiles_n, t)) return;
   const int nrb = (t.rows + 31) >> 5;
   switch (nrb) {
-    case 1: gemm_tile<1, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
-    case 2: if constexpr (RB >= 2) gemm_tile<2, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
-    case 3: if constexpr (RB >= 3) gemm_tile<3, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
-    case 4: if constexpr (RB >= 4) gemm_tile<4, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
-    case 5: if constexpr (RB >= 5) gemm_tile<5, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
-    case 6: if constexpr (RB >= 6) gemm_tile<6, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
-    case 7: if constexpr (RB >= 7) gemm_tile<7, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
-    default: if constexpr (RB >= 8) gemm_tile<8, RB, EPI, AMODE, SB, KT>(a, t, smem); break;
+    case 1: gemm_tile<1, RB, EPI, AMODE, KT>(a, t, smem); break;
+    case 2: if constexpr (RB >= 2) gemm_tile<2, RB, EPI, AMODE, KT>(a, t, smem); break;
+    case 3: if constexpr (RB >= 3) gemm_tile<3, RB, EPI, AMODE, KT>(a, t, smem); break;
+    case 4: if constexpr (RB >= 4) gemm_tile<4, RB, EPI, AMODE, KT>(a, t, smem); break;
+    case 5: if constexpr (RB >= 5) gemm_tile<5, RB, EPI, AMODE, KT>(a, t, smem); break;
+    case 6: if constexpr (RB >= 6) gemm_tile<6, RB, EPI, AMODE, KT>(a, t, smem); break;
+    case 7: if constexpr (RB >= 7) gemm_tile<7, RB, EPI, AMODE, KT>(a, t, smem); break;
+    default: if constexpr (RB >= 8) gemm_tile<8, RB, EPI, AMODE, KT>(a, t, smem); break;
   }
 }
 
 template <int RB, int EPI, int AMODE, bool KT>
 hipError_t launch_rb(const GemmArgs& a, int64_t mt_cap, hipStream_t s) {
-  // weight stages: as deep as the 160 KB of LDS allows next to the activations
-  constexpr int SB = (RB >= 8) ? 3 : 4;
   constexpr int CPW = (EPI == EPI_GATE_UP) ? 32 : 64;
   const int64_t n_tiles_n = (a.n_cols + kWaves * CPW - 1) / (kWaves * CPW);
   const int64_t mt = a.seg_off ? mt_cap : (a.dense_rows + RB * 32 - 1) / (RB * 32);
   const int64_t grid = gemm::round8(mt * n_tiles_n);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  moe_gemm_bf16<RB, EPI, AMODE, SB, KT><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a, n_tiles_n);
+  moe_gemm_bf16<RB, EPI, AMODE, KT><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a, n_tiles_n);
   return hipGetLastError();
 }
 
