@@ -272,6 +272,7 @@ hipError_t grouped_gemm(const moe_config* c, const Plan& p, int64_t N, const voi
   a.n_cols = n_cols;
   a.seg_off = seg_off;
   a.mt_off = at<int32_t>(ws, p.mt_off);
+  a.n_seg = c->n_experts;
   a.tile_seg = at<int32_t>(ws, p.tile_seg);
   a.tile_cap = p.tile_cap;
   a.C = C;

@@ -63,6 +63,7 @@ struct GemmArgs {
   const int32_t* seg_off; // [S+1] segment row offsets, or null for one dense segment
   int64_t dense_rows;     // rows of the dense segment (seg_off == null)
   const int32_t* mt_off;  // [S+1] m-tile prefix (grouped only)
+  int64_t n_seg;          // S, segments (grouped only)
   const int32_t* tile_seg;// m-tile -> segment, -1 past the last (grouped only)
   int64_t tile_cap;       // entries of tile_seg
   void* C;                // output

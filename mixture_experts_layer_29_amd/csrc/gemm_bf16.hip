@@ -392,7 +392,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void moe_gemm_bf16(GemmArgs a, int64_t n_tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<RB>::kBytes];
   TileLoc t;
-  if (!gemm::locate<RB * 32>(a, gemm::remap_xcd(blockIdx.x, gridDim.x), n_tiles_n, t)) return;
+  const int64_t L = gemm::tile_of_block<RB * 32>(a, blockIdx.x, n_tiles_n);
+  if (L < 0 || !gemm::locate<RB * 32>(a, L, n_tiles_n, t)) return;
   const int nrb = (t.rows + 31) >> 5;
   switch (nrb) {
     case 1: gemm_tile<1, RB, EPI, AMODE, KT>(a, t, smem); break;
@@ -418,7 +419,7 @@ hipError_t launch_rb(const GemmArgs& a, int64_t mt_cap, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile heights: rb in {1, 2, 4, 8} row blocks of 32.  A K that is not a
+// Tile heights: rb in {1, 2, 4, 6, 8} row blocks of 32.  A K that is not a
 // multiple of 64 (odd shapes only) runs the clamped variant, with rb = 1.
 template <int EPI, int AMODE>
 hipError_t launch_any(const GemmArgs& a, int rb, int64_t mt_cap, hipStream_t s) {
@@ -434,6 +435,9 @@ hipError_t launch_any(const GemmArgs& a, int rb, int64_t mt_cap, hipStream_t s) 
     case 2: return launch_rb<2, EPI, AMODE, false>(a, mt_cap, s);
     case 4:
       if constexpr (AMODE != A_REPEAT) return launch_rb<4, EPI, AMODE, false>(a, mt_cap, s);
+      return hipErrorInvalidValue;
+    case 6:
+      if constexpr (AMODE != A_REPEAT) return launch_rb<6, EPI, AMODE, false>(a, mt_cap, s);
       return hipErrorInvalidValue;
     case 8:
       if constexpr (AMODE != A_REPEAT) return launch_rb<8, EPI, AMODE, false>(a, mt_cap, s);

@@ -7,12 +7,22 @@
 namespace moe {
 namespace gemm {
 
-// Work-groups are dispatched to the 8 XCDs round-robin (id % 8).  Logical tile
-// L = (id % 8) * (grid / 8) + id / 8 gives each XCD a contiguous run of tiles.
-// The grid is a multiple of 8.
-__device__ __forceinline__ int64_t remap_xcd(int64_t bid, int64_t nwg) {
-  const int64_t per = nwg >> 3;
-  return (bid & 7) * per + (bid >> 3);
+// Work-groups are dispatched to the 8 XCDs round-robin (id % 8).  The grid of a
+// grouped product is sized for the most m-tiles the routing can produce, while
+// the tiles that exist (T, known on the device only) are numbered from 0; so
+// the T tiles are split into 8 contiguous runs of ceil(T/8), and work-group id
+// takes tile (id % 8) * ceil(T/8) + id / 8: every XCD gets an equal, contiguous
+// share (consecutive tiles share weights or activations in its L2).  Returns
+// -1 for a work-group with no tile.  The grid holds at least 8 * ceil(T/8).
+template <int BM>
+__device__ __forceinline__ int64_t tile_of_block(const GemmArgs& a, int64_t bid, int64_t n_tiles_n) {
+  const int64_t T = a.seg_off ? (int64_t)a.mt_off[a.n_seg] * n_tiles_n
+                              : (a.dense_rows + BM - 1) / BM * n_tiles_n;
+  const int64_t per = (T + 7) >> 3;
+  const int64_t i = bid >> 3;
+  if (i >= per) return -1;
+  const int64_t L = (bid & 7) * per + i;
+  return L < T ? L : -1;
 }
 
 // Expert activations (Kimi K3 "Gate features" page: expert and situ excerpts):

@@ -19,7 +19,8 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_f32(GemmArgs a, int64_t n_t
   __shared__ float Bs[2][16][64 + 1];
   const int tid = threadIdx.x;
   TileLoc t;
-  if (!gemm::locate<kRows>(a, gemm::remap_xcd(blockIdx.x, gridDim.x), n_tiles_n, t)) return;
+  const int64_t L = gemm::tile_of_block<kRows>(a, blockIdx.x, n_tiles_n);
+  if (L < 0 || !gemm::locate<kRows>(a, L, n_tiles_n, t)) return;
   const int64_t K = a.K;
   const int tx = tid & 15, ty = tid >> 4;
   const int64_t col0 = t.j * 64;
