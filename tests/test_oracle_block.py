@@ -236,3 +236,52 @@ def test_shared_expert_adds_on_full_input():
     y = oracle.block_tokens(cfg, W, x, np.arange(5), idx, np.ones((5, 1)))
     y_routed = oracle.block_tokens(dict(cfg, d_sh=0), W, x, np.arange(5), idx, np.ones((5, 1)))
     np.testing.assert_allclose(y, 2.0 * y_routed, rtol=1e-13)
+
+
+# ---- the row stages the GPU parity tests use ------------------------------
+
+@pytest.mark.parametrize("name", ["silu", "situ", "situ_no_linear_beta", "k1"])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_row_stages_compose_to_the_block(name, bf16):
+    """gate_up_rows, down_rows and combine over the sorted dispatch give the
+    per-token oracle's y (itself pinned to the masked dense formulation above),
+    with a residual added once; gate_up_rows alone equals torch's float64
+    linear + activation on each row's own expert."""
+    cfg = CASES[name]
+    rng = np.random.default_rng(31 + len(name) + bf16)
+    N, k = 25, cfg["k"]
+    x, W, idx, w = _make(rng, N, cfg, bf16)
+    w32 = w.astype(np.float32).astype(np.float64)  # combine takes fp32 weights
+    counts, offsets, perm, inv = oracle.counts_perm(idx, cfg["E"])
+    xs = x[perm // k]
+    expert = np.repeat(np.arange(cfg["E"]), counts).astype(np.int32)
+    h = oracle.gate_up_rows(cfg, W["w1"], W["w3"], xs, expert)
+    # the stages store h and the expert outputs in the weights' type (fp32 or
+    # bf16, as the GPU path does), so the composition carries those roundings
+    def store(a):
+        a = a.astype(np.float32)
+        return synth.f32_to_bf16_bits(a).reshape(a.shape) if bf16 else a
+
+    h32 = store(h)
+    out = oracle.down_rows(cfg, W["w2"], h32, expert)
+    res = store(rng.normal(0, 1, (N, cfg["d"])))
+    y = oracle.combine(store(out), inv, w32.astype(np.float32), res)
+    ref = oracle.block_tokens(cfg, W, x, np.arange(N), idx, w32) + _t(res).numpy()
+    if bf16:
+        assert np.linalg.norm(y - ref) <= 1e-2 * np.linalg.norm(ref)
+    else:
+        np.testing.assert_allclose(y, ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+
+    X = _t(xs)
+    for r in range(0, xs.shape[0], 7):
+        e = expert[r]
+        g = F.linear(X[r], _t(W["w1"][e]))
+        u = F.linear(X[r], _t(W["w3"][e]))
+        if cfg["act"] == "silu":
+            hr = F.silu(g) * u
+        else:
+            b, lb = cfg["situ_beta"], cfg["situ_linear_beta"]
+            hr = b * torch.tanh(g / b) * torch.sigmoid(g) * (lb * torch.tanh(u / lb) if lb > 0 else u)
+        np.testing.assert_allclose(h[r], hr.numpy(), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(out[r], F.linear(_t(h32[r]), _t(W["w2"][e])).numpy(),
+                                   rtol=1e-12, atol=1e-14)

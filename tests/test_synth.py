@@ -97,3 +97,16 @@ def test_zipf_profile():
     assert np.array_equal(np.sort(b), want)
     assert not np.array_equal(b, (0.25 * ranks ** -1.1).astype(np.float32))  # shuffled
     assert np.array_equal(b, synth.zipf_bias(E, 0))
+
+
+def test_workload_sizes_match_page_shapes():
+    """Every size the pages print (tests/golden/page_shapes.json, each with its
+    citation) is the size of the workloads built on it."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "page_shapes.json")
+    facts = json.load(open(path))["facts"]
+    assert facts
+    for f in facts:
+        for name in f["workloads"]:
+            assert getattr(synth.WORKLOADS[name], f["field"]) == f["value"], (name, f["what"])
