@@ -123,6 +123,8 @@ struct Plan {
   int64_t tile_cap = 0;
   int64_t dp = 0;          // router width padded to 64
   int64_t n_chunks = 0;
+  int router_rb = 1;       // router product (bf16): tile height in row blocks,
+  int64_t router_splits = 1, router_split_blocks = 0;  // and its K ranges
 };
 
 struct Carver {
@@ -159,6 +161,27 @@ int dense_rb(int64_t rows, int64_t K) {
   return 1;
 }
 
+// Router product (bf16 path): [N, 3 dp] x [E, 3 dp]^T, tiles of rb*32 rows by
+// 256 experts.  There are few such tiles (N/256 at prefill, 8 at decode) and
+// each would stream all of W_r, so K is cut into ranges (at least 8 blocks of
+// 64 each) until the tiles and ranges fill the GPU once; the selection kernel
+// adds the partial products in range order.
+void plan_router(const moe_config* c, int64_t N, Plan& p) {
+  const int64_t nkb = 3 * p.dp / 64;
+  p.router_rb = N >= 4096 ? 8 : (N >= 1024 ? 4 : (N >= 256 ? 2 : 1));
+  p.router_splits = 1;
+  p.router_split_blocks = nkb;
+  if (!is_bf16(c)) return;
+  const int64_t mt = (N + p.router_rb * 32 - 1) / (p.router_rb * 32);
+  const int64_t tiles = mt * ((c->n_experts + 255) / 256);
+  if (tiles <= 0 || tiles >= 256) return;
+  int64_t want = (256 + tiles - 1) / tiles;
+  const int64_t most = nkb / 8 > 1 ? nkb / 8 : 1;
+  if (want > most) want = most;
+  p.router_split_blocks = (nkb + want - 1) / want;
+  p.router_splits = (nkb + p.router_split_blocks - 1) / p.router_split_blocks;
+}
+
 Plan make_plan(const moe_config* c, int64_t N, int call) {
   Plan p;
   const int64_t E = c->n_experts, k = c->top_k, S = N * k;
@@ -168,11 +191,12 @@ Plan make_plan(const moe_config* c, int64_t N, int call) {
   p.tile_cap = S / p.rows_per_tile + (E < S ? E : S) + 1;
   p.dp = (c->d + 63) / 64 * 64;
   p.n_chunks = (N + 63) / 64;
+  plan_router(c, N, p);
   Carver cv;
   const bool block = call == MOE_CALL_BLOCK;
   if (call == MOE_CALL_ROUTE || block) {
     if (is_bf16(c)) p.w_split = cv.take((size_t)E * 3 * p.dp * 2);
-    p.logits = cv.take((size_t)N * E * 4);
+    p.logits = cv.take((size_t)p.router_splits * N * E * 4);
   }
   if (call == MOE_CALL_PERMUTE || block) {
     p.bits = cv.take((size_t)p.n_chunks * E * 8);
@@ -306,12 +330,15 @@ moe_status run_route(const moe_config* c, int64_t N, const void* hidden, const f
     a.C = logits;
     a.ldc = E;
     a.c_rows = N;
-    // one n-tile spans 256 experts, so short m-tiles are what fills the GPU
-    CHECK_HIP(moe::launch_gemm_bf16(a, moe::EPI_STORE_F32, moe::A_REPEAT, N > 4096 ? 2 : 1, 0, s));
+    a.k_splits = p.router_splits;
+    a.k_split_blocks = p.router_split_blocks;
+    a.c_split_stride = N * E;
+    CHECK_HIP(moe::launch_gemm_bf16(a, moe::EPI_STORE_F32, moe::A_REPEAT, p.router_rb, 0, s));
   } else {
     CHECK_HIP(dense_gemm(c, hidden, N, c->d, w_router, nullptr, E, logits, moe::EPI_STORE, nullptr, s));
   }
-  CHECK_HIP(moe::launch_route_select(logits, bias, N, E, c->n_group, c->topk_group, c->top_k,
+  const int parts = is_bf16(c) ? (int)p.router_splits : 1;
+  CHECK_HIP(moe::launch_route_select(logits, parts, N * E, bias, N, E, c->n_group, c->topk_group, c->top_k,
                                      c->norm_topk_prob ? 1 : 0, c->route_scale, idx, wts, s));
   return MOE_OK;
 }

@@ -62,6 +62,9 @@ struct GemmArgs {
   int64_t n_cols;         // output columns per segment
   const int32_t* seg_off; // [S+1] segment row offsets, or null for one dense segment
   int64_t dense_rows;     // rows of the dense segment (seg_off == null)
+  int64_t k_splits;       // dense only: K is cut into this many ranges (0 or 1: none),
+  int64_t k_split_blocks; //   each of this many 64-wide blocks, every range non-empty;
+  int64_t c_split_stride; //   range s writes its partial product at C + s * c_split_stride
   const int32_t* mt_off;  // [S+1] m-tile prefix (grouped only)
   int64_t n_seg;          // S, segments (grouped only)
   const int32_t* tile_seg;// m-tile -> segment, -1 past the last (grouped only)
@@ -88,7 +91,8 @@ int gemm_f32_rows_per_tile();
 // Router.
 hipError_t launch_router_split(const float* w_router, int64_t E, int64_t d, int64_t dp,
                                bf16_t* w_split, hipStream_t s);
-hipError_t launch_route_select(const float* logits, const float* bias, int64_t N, int64_t E,
+hipError_t launch_route_select(const float* logits, int n_parts, int64_t part_stride,
+                               const float* bias, int64_t N, int64_t E,
                                int G, int TG, int k, int norm, float scale, int32_t* topk_idx,
                                float* topk_weight, hipStream_t s);
 

@@ -129,8 +129,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int64_t K = a.K;
-  const int64_t nkb = (K + 63) >> 6;
+  const int64_t K = a.K;                // row length of both operands
+  const int64_t kbase = t.kb0;          // the tile's K range: blocks kbase .. kbase+nkb-1
+  const int64_t nkb = t.kb1 - t.kb0;
   const int slot = lane & 7;  // LDS chunk slot this lane's load lands in
 
   // ---- weights: sub-block (kb, c) holds the 32 rows of column block c of the
@@ -167,10 +168,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
   }
   const int64_t a_per_blocks = AMODE == A_REPEAT ? (a.a_period >> 6) : 1;
 
-  // block indices are clamped to [0, nkb): a load past either end fetches a
-  // real block again, into a stage that nobody reads before it is refilled
+  // block indices (relative to kbase) are clamped to [0, nkb): a load past
+  // either end fetches a real block again, into a stage that nobody reads
+  // before it is refilled
   auto issue_a = [&](int64_t kb, int stage) {
-    kb = kb < 0 ? 0 : (kb >= nkb ? nkb - 1 : kb);
+    kb = kbase + (kb < 0 ? 0 : (kb >= nkb ? nkb - 1 : kb));
     const int64_t col = (AMODE == A_REPEAT ? (kb % a_per_blocks) : kb) * 64;
     uint8_t* const dst = As + stage * ATILE + wave * NR * 1024;
 #pragma unroll
@@ -184,7 +186,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
     }
   };
   auto issue_b = [&](int64_t kb, int cblk, int stage) {
-    kb = kb >= nkb ? nkb - 1 : kb;
+    kb = kbase + (kb >= nkb ? nkb - 1 : kb);
     uint8_t* const dst = Bs + stage * kBStage + wave * kBWave;
 #pragma unroll
     for (int i = 0; i < kBLoads; ++i) {
@@ -199,7 +201,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
     uint8_t* const dst = As + stage * ATILE + wave * NR * 1024;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      if (kb * 64 + achunk[i] * 8 >= K)
+      if ((kbase + kb) * 64 + achunk[i] * 8 >= K)
         *reinterpret_cast<u32x4*>(dst + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
     }
     wait_lgkm0();
@@ -353,8 +355,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
           f32x4 v0 = *reinterpret_cast<const f32x4*>(&S[wave][row][cc * 8]);
           f32x4 v1 = *reinterpret_cast<const f32x4*>(&S[wave][row][cc * 8 + 4]);
           if (EPI == EPI_STORE_F32) {
-            // router logits: any expert count, so scalar stores up to n_cols
-            float* dst = static_cast<float*>(a.C) + orow * a.ldc + col;
+            // router logits: any expert count, so scalar stores up to n_cols;
+            // a split-K range writes its own partial product
+            float* dst = static_cast<float*>(a.C) + t.split * a.c_split_stride + orow * a.ldc + col;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               if (col + e < a.n_cols) dst[e] = e < 4 ? v0[e] : v1[e - 4];
@@ -411,7 +414,9 @@ template <int RB, int EPI, int AMODE, bool KT>
 hipError_t launch_rb(const GemmArgs& a, int64_t mt_cap, hipStream_t s) {
   constexpr int CPW = (EPI == EPI_GATE_UP) ? 32 : 64;
   const int64_t n_tiles_n = (a.n_cols + kWaves * CPW - 1) / (kWaves * CPW);
-  const int64_t mt = a.seg_off ? mt_cap : (a.dense_rows + RB * 32 - 1) / (RB * 32);
+  const int64_t mt = a.seg_off ? mt_cap
+                              : (a.dense_rows + RB * 32 - 1) / (RB * 32) *
+                                    (a.k_splits > 1 ? a.k_splits : 1);
   const int64_t grid = gemm::round8(mt * n_tiles_n);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
@@ -433,15 +438,11 @@ hipError_t launch_any(const GemmArgs& a, int rb, int64_t mt_cap, hipStream_t s) 
   switch (rb) {
     case 1: return launch_rb<1, EPI, AMODE, false>(a, mt_cap, s);
     case 2: return launch_rb<2, EPI, AMODE, false>(a, mt_cap, s);
-    case 4:
-      if constexpr (AMODE != A_REPEAT) return launch_rb<4, EPI, AMODE, false>(a, mt_cap, s);
-      return hipErrorInvalidValue;
+    case 4: return launch_rb<4, EPI, AMODE, false>(a, mt_cap, s);
     case 6:
       if constexpr (AMODE != A_REPEAT) return launch_rb<6, EPI, AMODE, false>(a, mt_cap, s);
       return hipErrorInvalidValue;
-    case 8:
-      if constexpr (AMODE != A_REPEAT) return launch_rb<8, EPI, AMODE, false>(a, mt_cap, s);
-      return hipErrorInvalidValue;
+    case 8: return launch_rb<8, EPI, AMODE, false>(a, mt_cap, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -17,7 +17,8 @@ namespace gemm {
 template <int BM>
 __device__ __forceinline__ int64_t tile_of_block(const GemmArgs& a, int64_t bid, int64_t n_tiles_n) {
   const int64_t T = a.seg_off ? (int64_t)a.mt_off[a.n_seg] * n_tiles_n
-                              : (a.dense_rows + BM - 1) / BM * n_tiles_n;
+                              : (a.dense_rows + BM - 1) / BM * n_tiles_n *
+                                    (a.k_splits > 1 ? a.k_splits : 1);
   const int64_t per = (T + 7) >> 3;
   const int64_t i = bid >> 3;
   if (i >= per) return -1;
@@ -37,15 +38,19 @@ __device__ __forceinline__ float act_pair(int act, float g, float u, float beta,
 
 struct TileLoc {
   int64_t seg;
-  int64_t row0;  // first row of the tile in the concatenated row space
-  int rows;      // rows of the tile that exist (1 .. BM)
-  int64_t j;     // n-tile
+  int64_t row0;   // first row of the tile in the concatenated row space
+  int rows;       // rows of the tile that exist (1 .. BM)
+  int64_t j;      // n-tile
+  int64_t split;  // K range (dense split-K), else 0
+  int64_t kb0;    // first 64-wide K block of the tile's K range
+  int64_t kb1;    // one past its last block
 };
 
-// Logical tile L -> (segment, m-tile, n-tile).  Grouped: tiles are numbered
-// segment by segment; inside a segment n-tile-major with the m-tiles adjacent,
-// so the m-tiles that share one weight tile run side by side.  Dense: the same
-// with one segment.  False when L is past the last tile.
+// Logical tile L -> (segment, m-tile, n-tile, K range).  Grouped: tiles are
+// numbered segment by segment; inside a segment n-tile-major with the m-tiles
+// adjacent, so the m-tiles that share one weight tile run side by side.
+// Dense: the same with one segment, repeated for each K range of a split-K
+// product.  False when L is past the last tile.
 template <int BM>
 __device__ __forceinline__ bool locate(const GemmArgs& a, int64_t L, int64_t n_tiles_n,
                                        TileLoc& t) {
@@ -64,16 +69,27 @@ __device__ __forceinline__ bool locate(const GemmArgs& a, int64_t L, int64_t n_t
     t.row0 = s0 + i * BM;
     t.rows = (int)min((int64_t)BM, s1 - t.row0);
     t.j = j;
+    t.split = 0;
+    t.kb0 = 0;
+    t.kb1 = (a.K + 63) >> 6;
     return t.row0 >= 0 && t.rows > 0;
   }
   const int64_t mt = (a.dense_rows + BM - 1) / BM;
-  if (L >= mt * n_tiles_n) return false;
+  const int64_t per_split = mt * n_tiles_n;
+  const int64_t splits = a.k_splits > 1 ? a.k_splits : 1;
+  if (L >= per_split * splits) return false;
+  const int64_t q = L / per_split;
+  L -= q * per_split;
   const int64_t j = L / mt, i = L - j * mt;
+  const int64_t nkb = (a.K + 63) >> 6;
   t.seg = 0;
   t.row0 = i * BM;
   t.rows = (int)min((int64_t)BM, a.dense_rows - t.row0);
   t.j = j;
-  return true;
+  t.split = q;
+  t.kb0 = splits > 1 ? q * a.k_split_blocks : 0;
+  t.kb1 = splits > 1 ? min(nkb, t.kb0 + a.k_split_blocks) : nkb;
+  return t.kb1 > t.kb0;
 }
 
 inline int64_t round8(int64_t n) { return (n + 7) & ~(int64_t)7; }

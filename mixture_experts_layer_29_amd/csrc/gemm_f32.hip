@@ -109,6 +109,7 @@ hipError_t launch(const GemmArgs& a, int64_t mt_cap, hipStream_t s) {
 int gemm_f32_rows_per_tile() { return kRows; }
 
 hipError_t launch_gemm_f32(const GemmArgs& a, int epi, int amode, int64_t mt_cap, hipStream_t s) {
+  if (a.k_splits > 1) return hipErrorInvalidValue;  // split-K is a bf16-path option only
   if (epi == EPI_GATE_UP && amode == A_DIRECT) return launch<EPI_GATE_UP, A_DIRECT>(a, mt_cap, s);
   if (epi == EPI_GATE_UP && amode == A_GATHER) return launch<EPI_GATE_UP, A_GATHER>(a, mt_cap, s);
   if ((epi == EPI_STORE || epi == EPI_STORE_F32) && amode == A_DIRECT)

@@ -69,7 +69,8 @@ constexpr int kMaxG = 1024;
 // One token per wave; P = values per lane (expert e = i * 64 + lane).
 template <int P>
 __global__ __launch_bounds__(kThreads) void moe_route_select(
-    const float* __restrict__ logits, const float* __restrict__ bias, int64_t N, int E, int G,
+    const float* __restrict__ logits, int n_parts, int64_t part_stride,
+    const float* __restrict__ bias, int64_t N, int E, int G,
     int TG, int k, int norm, float scale, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_weight) {
   __shared__ float sh_b[4][kMaxG];   // choice values (group stage only)
@@ -83,7 +84,10 @@ __global__ __launch_bounds__(kThreads) void moe_route_select(
   for (int i = 0; i < P; ++i) {
     const int e = i * 64 + lane;
     if (live && e < E) {
-      const float l = logits[n * E + e];
+      // the router product may arrive as partial sums over K ranges: added
+      // in range order, so the logit does not depend on the launch
+      float l = logits[n * E + e];
+      for (int q = 1; q < n_parts; ++q) l += logits[q * part_stride + n * E + e];
       s[i] = 1.0f / (1.0f + expf(-l));
       b[i] = s[i] + bias[e];
     } else {
@@ -210,12 +214,12 @@ __global__ __launch_bounds__(kThreads) void moe_route_select(
 }
 
 template <int P>
-hipError_t launch_select(const float* logits, const float* bias, int64_t N, int64_t E, int G,
-                         int TG, int k, int norm, float scale, int32_t* idx, float* w,
-                         hipStream_t s) {
+hipError_t launch_select(const float* logits, int n_parts, int64_t part_stride, const float* bias,
+                         int64_t N, int64_t E, int G, int TG, int k, int norm, float scale,
+                         int32_t* idx, float* w, hipStream_t s) {
   const int64_t grid = (N + 3) / 4;
   moe_route_select<P><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(
-      logits, bias, N, (int)E, G, TG, k, norm, scale, idx, w);
+      logits, n_parts, part_stride, bias, N, (int)E, G, TG, k, norm, scale, idx, w);
   return hipGetLastError();
 }
 
@@ -230,16 +234,22 @@ hipError_t launch_router_split(const float* w_router, int64_t E, int64_t d, int6
   return hipGetLastError();
 }
 
-hipError_t launch_route_select(const float* logits, const float* bias, int64_t N, int64_t E,
+hipError_t launch_route_select(const float* logits, int n_parts, int64_t part_stride,
+                               const float* bias, int64_t N, int64_t E,
                                int G, int TG, int k, int norm, float scale, int32_t* topk_idx,
                                float* topk_weight, hipStream_t s) {
   if (N == 0) return hipSuccess;
+  if (n_parts < 1) return hipErrorInvalidValue;
   const int64_t P = (E + 63) / 64;
-  if (P <= 1) return launch_select<1>(logits, bias, N, E, G, TG, k, norm, scale, topk_idx, topk_weight, s);
-  if (P <= 2) return launch_select<2>(logits, bias, N, E, G, TG, k, norm, scale, topk_idx, topk_weight, s);
-  if (P <= 4) return launch_select<4>(logits, bias, N, E, G, TG, k, norm, scale, topk_idx, topk_weight, s);
-  if (P <= 8) return launch_select<8>(logits, bias, N, E, G, TG, k, norm, scale, topk_idx, topk_weight, s);
-  if (P <= 16) return launch_select<16>(logits, bias, N, E, G, TG, k, norm, scale, topk_idx, topk_weight, s);
+#define MOE_SELECT(PP)                                                                       \
+  return launch_select<PP>(logits, n_parts, part_stride, bias, N, E, G, TG, k, norm, scale, \
+                           topk_idx, topk_weight, s)
+  if (P <= 1) MOE_SELECT(1);
+  if (P <= 2) MOE_SELECT(2);
+  if (P <= 4) MOE_SELECT(4);
+  if (P <= 8) MOE_SELECT(8);
+  if (P <= 16) MOE_SELECT(16);
+#undef MOE_SELECT
   return hipErrorInvalidValue;
 }
 
