@@ -47,8 +47,6 @@
 // Inside a 64-wide K block the lanes visit K in an order of our choosing, the
 // same for both operands (lane half h takes elements 32h .. 32h+31, eight per
 // MFMA step).
-#include <type_traits>
-
 #include "gemm_common.h"
 
 namespace moe {
@@ -218,30 +216,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
   }
 
   // One column sub-block from LDS: 4 MFMA steps; in step s lane half h reads
-  // chunk 4h + s of its rows.  Step s+1's fragments are read between step s's
-  // MFMAs (a wave issues an MFMA only every few dozen cycles).
+  // chunk 4h + s of its rows.  The activation fragments of a K block are read
+  // from LDS once, in its first sub-block, and kept in registers for the
+  // second (LDS bandwidth is shared with the load units' writes).  Step s+1's
+  // fragments are read between step s's MFMAs (a wave issues an MFMA only
+  // every few dozen cycles).
   const int rsel = lane & 31;
   const int cbase = (lane >> 5) * 4;
-  auto compute = [&](auto cblk_tag, const uint8_t* at, const uint8_t* bt) {
-    constexpr int C = decltype(cblk_tag)::value;
-    bf16x8 af[2][NR];
+  bf16x8 afk[4][NR];  // activation fragments of the current K block
+  auto compute0 = [&](const uint8_t* at, const uint8_t* bt) {
     bf16x8 bf[2];
-    auto read_frags = [&](int s, bf16x8 (&fa)[NR], bf16x8& fb) {
+    auto read_frags = [&](int s, bf16x8& fb) {
       const int c = cbase + s;
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb) {
-        fa[rb] = *reinterpret_cast<const bf16x8*>(at + swz(rb * 32 + rsel, c));
+        afk[s][rb] = *reinterpret_cast<const bf16x8*>(at + swz(rb * 32 + rsel, c));
       }
       fb = *reinterpret_cast<const bf16x8*>(bt + swz(rsel, c));
     };
-    read_frags(0, af[0], bf[0]);
+    read_frags(0, bf[0]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (s < 3) read_frags(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+      if (s < 3) read_frags(s + 1, bf[(s + 1) & 1]);
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb) {
-        acc[rb][C] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][rb], bf[s & 1], acc[rb][C], 0, 0, 0);
+        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afk[s][rb], bf[s & 1], acc[rb][0], 0, 0, 0);
       }
       if (s < 3) {
         // MFMA, read, MFMA, read, ...: the reads hide under the MFMAs
@@ -255,12 +255,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  auto compute1 = [&](const uint8_t* bt) {
+    bf16x8 bf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bf[s] = *reinterpret_cast<const bf16x8*>(bt + swz(rsel, cbase + s));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int rb = 0; rb < NR; ++rb) {
+        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afk[s][rb], bf[s], acc[rb][1], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   // ---- pipeline over sub-iterations u = 2 kb + c.  Sub-iteration u (after
-  // its wait and barrier) issues, for even u only, A(kb + 1) into A stage
-  // (kb+1)&1, then sub-block u + SB - 1 into stage (u - 1) % SB: both stages
-  // were last read before the barrier.  The same happens for u = 1-SB .. -1
-  // before the loop (the prologue; A blocks below 0 fetch A(0) again).
+  // its wait) issues, for even u only, A(kb + 1) into A stage (kb+1)&1, then
+  // sub-block u + SB - 1 into stage (u - 1) % SB.  A wave reads only its own
+  // slice of a weight stage, so its own program order protects the slice it
+  // refills; the activation tile is shared, so even u has a work-group barrier
+  // between the wait and the issue (every wave's part of A(kb) has landed, and
+  // every wave has read A(kb-1), which its first sub-block keeps in registers).
+  // The same happens for u = 1-SB .. -1 before the loop (the prologue; A
+  // blocks below 0 fetch A(0) again).
   //  - even u needs A(kb) (issued at u-2) and sub-block u (issued at
   //    u-SB+1 <= u-3, hence older): the loads younger than A(kb) are the
   //    weight loads of u-2 and u-1, so at most 2 kBLoads may stay outstanding;
@@ -289,16 +307,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
       const int64_t ub = 2 * kb + SB - 1;
       issue_b(ub >> 1, (SB - 1) & 1, sb == 0 ? SB - 1 : sb - 1);
     }
-    compute(std::integral_constant<int, 0>{}, As + sa * ATILE, bt0 + sb * kBStage);
+    compute0(As + sa * ATILE, bt0 + sb * kBStage);
     sb = (sb + 1 == SB) ? 0 : sb + 1;
-    // c = 1
+    // c = 1: no barrier (the wave's own weight slice, A in registers)
     wait_vm<kWaitOdd>();
-    wg_barrier();
     {
       const int64_t ub = 2 * kb + SB;
       issue_b(ub >> 1, SB & 1, sb == 0 ? SB - 1 : sb - 1);
     }
-    compute(std::integral_constant<int, 1>{}, As + sa * ATILE, bt0 + sb * kBStage);
+    compute1(bt0 + sb * kBStage);
     sb = (sb + 1 == SB) ? 0 : sb + 1;
   }
   wait_vm<0>();
