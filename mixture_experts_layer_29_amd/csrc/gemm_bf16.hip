@@ -65,6 +65,7 @@ constexpr int kBLoads = kBRows / 8;                 // loads per wave per sub-bl
 constexpr int kBWave = kBRows * kRowBytes;          // 4 KB
 constexpr int kBStage = kWaves * kBWave;            // 16 KB
 constexpr int kLdsMax = 160 * 1024;                 // LDS of one CU
+constexpr int kCpolNT = 2;                          // cache policy bits of a load: nt
 constexpr int kLdsOut = 72;                         // fp32 per LDS epilogue row: 64 + 8 pad
 constexpr int kEpiBytes = kWaves * 32 * kLdsOut * 4;
 
@@ -183,6 +184,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
       __builtin_amdgcn_global_load_lds(MOE_GPTR(ap[i] + c), MOE_LPTR(dst + i * 1024), 16, 0, 0);
     }
   };
+  // Weights that only this launch reads (the routed experts') are loaded
+  // non-temporal, so they do not push the reused activation rows out of L2.
+  const bool b_nt = a.b_stream != 0;
   auto issue_b = [&](int64_t kb, int cblk, int stage) {
     kb = kbase + (kb >= nkb ? nkb - 1 : kb);
     uint8_t* const dst = Bs + stage * kBStage + wave * kBWave;
@@ -190,8 +194,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
     for (int i = 0; i < kBLoads; ++i) {
       int64_t off = kb * 64;
       if (KT) off = min(off, K - 8 - bchunk[i] * 8);  // A is zero there
-      __builtin_amdgcn_global_load_lds(MOE_GPTR(brow[cblk][i] + off), MOE_LPTR(dst + i * 1024), 16,
-                                       0, 0);
+      if (b_nt) {
+        __builtin_amdgcn_global_load_lds(MOE_GPTR(brow[cblk][i] + off), MOE_LPTR(dst + i * 1024),
+                                         16, 0, kCpolNT);
+      } else {
+        __builtin_amdgcn_global_load_lds(MOE_GPTR(brow[cblk][i] + off), MOE_LPTR(dst + i * 1024),
+                                         16, 0, 0);
+      }
     }
   };
   // K tail: zero this lane's activation chunks of the last block that lie past K
@@ -270,28 +279,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- pipeline over sub-iterations u = 2 kb + c.  Sub-iteration u (after
-  // its wait) issues, for even u only, A(kb + 1) into A stage (kb+1)&1, then
-  // sub-block u + SB - 1 into stage (u - 1) % SB.  A wave reads only its own
-  // slice of a weight stage, so its own program order protects the slice it
-  // refills; the activation tile is shared, so even u has a work-group barrier
-  // between the wait and the issue (every wave's part of A(kb) has landed, and
-  // every wave has read A(kb-1), which its first sub-block keeps in registers).
-  // The same happens for u = 1-SB .. -1 before the loop (the prologue; A
-  // blocks below 0 fetch A(0) again).
-  //  - even u needs A(kb) (issued at u-2) and sub-block u (issued at
-  //    u-SB+1 <= u-3, hence older): the loads younger than A(kb) are the
-  //    weight loads of u-2 and u-1, so at most 2 kBLoads may stay outstanding;
-  //  - odd u needs sub-block u: younger are the loads of u-SB+2 .. u-1, kBLoads
-  //    each plus NR at each of their ceil((SB-2)/2) even sub-iterations.
+  // ---- pipeline over sub-iterations u = 2 kb + c.  Sub-iteration u first
+  // issues sub-block u + SB - 1 into stage (u - 1) % SB, then waits for its
+  // own data; for even u it then passes a work-group barrier and issues
+  // A(kb + 1) into A stage (kb+1)&1.  A wave reads only its own slice of a
+  // weight stage, so its own program order protects the slice it refills (its
+  // reads of sub-block u - 1 are done); the activation tile is shared, so the
+  // barrier comes first (every wave's part of A(kb) has landed, and every wave
+  // has read A(kb-1), which its first sub-block keeps in registers).  The same
+  // issues happen for u = 1-SB .. -1 before the loop (the prologue; A blocks
+  // below 0 fetch A(0) again).
+  //  - even u needs A(kb) (issued at u-2, after that sub-iteration's weights)
+  //    and sub-block u (issued at u-SB+1 <= u-3, hence older): younger than
+  //    A(kb) are the weight loads of u-1 and u, 2 kBLoads;
+  //  - odd u needs sub-block u: younger are the A loads of u-SB+1 (when even),
+  //    and all loads of u-SB+2 .. u: kBLoads (SB-1) plus NR at each of the
+  //    floor(SB/2) even sub-iterations among u-SB+1 .. u-1.
   constexpr int kWaitEven = 2 * kBLoads;
-  constexpr int kWaitOdd = kBLoads * (SB - 2) + NR * ((SB - 1) / 2);
+  constexpr int kWaitOdd = kBLoads * (SB - 1) + NR * (SB / 2);
   static_assert(kWaitOdd < 64, "vmcnt range");
 #pragma unroll
   for (int q = 0; q < SB - 1; ++q) {
-    // u = q - (SB-1); A(u/2 + 1) <= A(0), all into stage 0 (same bytes)
+    // u = q - (SB-1): sub-block u + SB - 1 = q, then for even u A(u/2 + 1),
+    // which is at most A(0): all into stage 0 (same bytes)
+    issue_b(q >> 1, q & 1, q);
     if (((q + SB - 1) & 1) == 0) issue_a(0, 0);
-    issue_b(q >> 1, q & 1, q);  // sub-block u + SB - 1 = q
   }
 
   int sb = 0;  // stage of the sub-block being consumed
@@ -299,22 +311,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
   for (int64_t kb = 0; kb < nkb; ++kb) {
     const int sa = (int)(kb & 1);
     // c = 0
-    wait_vm<kWaitEven>();
-    if (KT && AMODE != A_REPEAT && kb == nkb - 1) zero_a_tail(kb, sa);
-    wg_barrier();
-    issue_a(kb + 1, sa ^ 1);
     {
       const int64_t ub = 2 * kb + SB - 1;
       issue_b(ub >> 1, (SB - 1) & 1, sb == 0 ? SB - 1 : sb - 1);
     }
+    wait_vm<kWaitEven>();
+    if (KT && AMODE != A_REPEAT && kb == nkb - 1) zero_a_tail(kb, sa);
+    wg_barrier();
+    issue_a(kb + 1, sa ^ 1);
     compute0(As + sa * ATILE, bt0 + sb * kBStage);
     sb = (sb + 1 == SB) ? 0 : sb + 1;
     // c = 1: no barrier (the wave's own weight slice, A in registers)
-    wait_vm<kWaitOdd>();
     {
       const int64_t ub = 2 * kb + SB;
       issue_b(ub >> 1, SB & 1, sb == 0 ? SB - 1 : sb - 1);
     }
+    wait_vm<kWaitOdd>();
     compute1(bt0 + sb * kBStage);
     sb = (sb + 1 == SB) ? 0 : sb + 1;
   }
