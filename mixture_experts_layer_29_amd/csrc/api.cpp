@@ -154,10 +154,17 @@ int choose_rb(const moe_config* c, int64_t N) {
   return 1;
 }
 
-int dense_rb(int64_t rows, int64_t K) {
+// Dense products (shared expert, latent projections) reuse every weight tile
+// across all m-tiles, so they are bound by the operand traffic into each CU
+// rather than by HBM: the tallest tile that still gives every CU a tile has
+// the most flops per byte loaded.
+int dense_rb(int64_t rows, int64_t K, int64_t n_cols, int epi) {
   if (K % 64) return 1;
-  if (rows >= 2048) return 4;
-  if (rows >= 512) return 2;
+  const int64_t cols_per_tile = epi == moe::EPI_GATE_UP ? 128 : 256;
+  const int64_t n_tiles = (n_cols + cols_per_tile - 1) / cols_per_tile;
+  for (int rb : {8, 4, 2}) {
+    if ((rows + rb * 32 - 1) / (rb * 32) * n_tiles >= 240) return rb;
+  }
   return 1;
 }
 
@@ -275,7 +282,7 @@ hipError_t dense_gemm(const moe_config* c, const void* A, int64_t rows, int64_t 
   a.act = c->act;
   a.beta = c->situ_beta > 0.0f ? c->situ_beta : 1.0f;
   a.lbeta = c->situ_linear_beta;
-  if (is_bf16(c)) return moe::launch_gemm_bf16(a, epi, moe::A_DIRECT, dense_rb(rows, K), 0, s);
+  if (is_bf16(c)) return moe::launch_gemm_bf16(a, epi, moe::A_DIRECT, dense_rb(rows, K, n_cols, epi), 0, s);
   return moe::launch_gemm_f32(a, epi, moe::A_DIRECT, 0, s);
 }
 
