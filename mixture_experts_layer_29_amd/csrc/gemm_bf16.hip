@@ -54,8 +54,24 @@ namespace {
 
 using gemm::TileLoc;
 
-#define MOE_GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
-#define MOE_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+// One wave-wide HBM->LDS copy: lane l's 16 bytes at `src` land at LDS byte
+// address m0 + 16 l (m0 = `lds`, uniform).  Written as inline asm on purpose:
+// the instruction has no register results (nothing for the compiler to track),
+// and the compiler, seeing an LDS-DMA load in flight, would otherwise treat
+// every LDS read as unordered and wait for all of them before each MFMA.  The
+// loads are counted by the explicit vmcnt waits of the pipeline below.
+template <bool NT>
+__device__ __forceinline__ void dma16(const void* src, const uint8_t* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>(lds));
+  if (NT) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(src), "s"(m0) : "memory", "m0");
+  } else {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(m0) : "memory", "m0");
+  }
+}
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -65,7 +81,6 @@ constexpr int kBLoads = kBRows / 8;                 // loads per wave per sub-bl
 constexpr int kBWave = kBRows * kRowBytes;          // 4 KB
 constexpr int kBStage = kWaves * kBWave;            // 16 KB
 constexpr int kLdsMax = 160 * 1024;                 // LDS of one CU
-constexpr int kCpolNT = 2;                          // cache policy bits of a load: nt
 constexpr int kLdsOut = 72;                         // fp32 per LDS epilogue row: 64 + 8 pad
 constexpr int kEpiBytes = kWaves * 32 * kLdsOut * 4;
 
@@ -181,7 +196,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
       // in LDS after the copy; either way the address stays inside the row
       if (AMODE == A_REPEAT) c = min(c, a.a_valid - 8 - achunk[i] * 8);
       else if (KT) c = min(c, K - 8 - achunk[i] * 8);
-      __builtin_amdgcn_global_load_lds(MOE_GPTR(ap[i] + c), MOE_LPTR(dst + i * 1024), 16, 0, 0);
+      dma16<false>(ap[i] + c, dst + i * 1024);
     }
   };
   // Weights that only this launch reads (the routed experts') are loaded
@@ -195,11 +210,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
       int64_t off = kb * 64;
       if (KT) off = min(off, K - 8 - bchunk[i] * 8);  // A is zero there
       if (b_nt) {
-        __builtin_amdgcn_global_load_lds(MOE_GPTR(brow[cblk][i] + off), MOE_LPTR(dst + i * 1024),
-                                         16, 0, kCpolNT);
+        dma16<true>(brow[cblk][i] + off, dst + i * 1024);
       } else {
-        __builtin_amdgcn_global_load_lds(MOE_GPTR(brow[cblk][i] + off), MOE_LPTR(dst + i * 1024),
-                                         16, 0, 0);
+        dma16<false>(brow[cblk][i] + off, dst + i * 1024);
       }
     }
   };
@@ -235,13 +248,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
   bf16x8 afk[4][NR];  // activation fragments of the current K block
   auto compute0 = [&](const uint8_t* at, const uint8_t* bt) {
     bf16x8 bf[2];
+    // weights first: MFMA rb then waits only for the reads up to A row block rb
     auto read_frags = [&](int s, bf16x8& fb) {
       const int c = cbase + s;
+      fb = *reinterpret_cast<const bf16x8*>(bt + swz(rsel, c));
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb) {
         afk[s][rb] = *reinterpret_cast<const bf16x8*>(at + swz(rb * 32 + rsel, c));
       }
-      fb = *reinterpret_cast<const bf16x8*>(bt + swz(rsel, c));
     };
     read_frags(0, bf[0]);
     __builtin_amdgcn_sched_barrier(0);
