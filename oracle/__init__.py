@@ -70,13 +70,14 @@ def _load():
         P = ctypes.c_void_p
         i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
         lib.oracle_num_threads.restype = i32
-        lib.oracle_router_scores.argtypes = [i64, i64, i64, P, i32, P, P, P, P, P]
+        lib.oracle_router_scores.argtypes = [i64, i64, i64, P, i32, P, P, i32, P, P, P]
         lib.oracle_router_scores.restype = i32
-        lib.oracle_select.argtypes = [i64, i32, i32, i32, P, P, P, P, P]
+        lib.oracle_select.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P]
         lib.oracle_select.restype = i32
         lib.oracle_weights.argtypes = [i32, i32, f64, P, P, P]
         lib.oracle_weights.restype = None
-        lib.oracle_route.argtypes = [i64, i64, i64, i32, i32, i32, i32, f64, P, i32, P, P, P, P, P]
+        lib.oracle_route.argtypes = [i64, i64, i64, i32, i32, i32, i32, f64, i32, P, i32, P, P, P,
+                                     P, P]
         lib.oracle_route.restype = i32
         lib.oracle_counts_perm.argtypes = [i64, i32, i64, P, P, P, P, P]
         lib.oracle_counts_perm.restype = i32
@@ -109,26 +110,39 @@ def _c(a: np.ndarray, dtype=None) -> np.ndarray:
     return np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
 
 
-def router_scores(x, w_router, bias):
-    """fp32 logits, scores and choice scores [N, E] as the pages compute them."""
+SCORE_FUNCS = {"sigmoid": 0, "softmax": 1}
+
+
+def _bias_ptr(bias):
+    """(array kept alive or None, pointer or None): a router may have no bias."""
+    if bias is None:
+        return None, None
+    b = _c(bias, np.float32)
+    return b, b.ctypes.data
+
+
+def router_scores(x, w_router, bias, score_func: str = "sigmoid"):
+    """fp32 logits, scores and choice scores [N, E] as the pages compute them
+    (bias None: a router without a bias, choice = score)."""
     x = _c(x)
     w_router = _c(w_router, np.float32)
-    bias = _c(bias, np.float32)
+    keep, bptr = _bias_ptr(bias)
     N, d = x.shape
     E = w_router.shape[0]
     logit = np.empty((N, E), np.float32)
     score = np.empty((N, E), np.float32)
     choice = np.empty((N, E), np.float32)
     rc = _load().oracle_router_scores(N, d, E, x.ctypes.data, _dtype_code(x), w_router.ctypes.data,
-                                      bias.ctypes.data, logit.ctypes.data, score.ctypes.data,
-                                      choice.ctypes.data)
+                                      bptr, SCORE_FUNCS[score_func], logit.ctypes.data,
+                                      score.ctypes.data, choice.ctypes.data)
     if rc:
         raise RuntimeError(f"oracle_router_scores failed ({rc})")
     return logit, score, choice
 
 
-def select(choice_row, G: int, TG: int, k: int):
-    """Group pruning + top-k on one token's fp32 choice scores.
+def select(choice_row, G: int, TG: int, k: int, group_by_max: bool = False):
+    """Group pruning + top-k on one token's fp32 choice scores (group score:
+    sum of the two largest, or the largest when group_by_max: no bias).
 
     Returns (idx ascending [k] int32, flags, gap_expert, gap_group, group_scores [G])."""
     choice_row = _c(choice_row, np.float32)
@@ -137,7 +151,8 @@ def select(choice_row, G: int, TG: int, k: int):
     ge = ctypes.c_double()
     gg = ctypes.c_double()
     gs = np.empty(G, np.float32)
-    f = _load().oracle_select(E, G, TG, k, choice_row.ctypes.data, idx.ctypes.data,
+    f = _load().oracle_select(E, G, TG, k, int(bool(group_by_max)), choice_row.ctypes.data,
+                              idx.ctypes.data,
                               ctypes.byref(ge), ctypes.byref(gg), gs.ctypes.data)
     if f < 0:
         raise ValueError("invalid routing configuration")
@@ -153,19 +168,22 @@ def weights(score_row, idx, norm_topk_prob: bool, route_scale: float):
     return out
 
 
-def route(x, w_router, bias, G: int, TG: int, k: int, norm_topk_prob: bool, route_scale: float):
-    """Router for all tokens: (topk_idx [N,k] int32 ascending, topk_weight [N,k] f64, flags [N])."""
+def route(x, w_router, bias, G: int, TG: int, k: int, norm_topk_prob: bool, route_scale: float,
+          score_func: str = "sigmoid"):
+    """Router for all tokens: (topk_idx [N,k] int32 ascending, topk_weight [N,k] f64, flags [N]).
+    bias None: a router without a bias (groups scored by their largest choice)."""
     x = _c(x)
     w_router = _c(w_router, np.float32)
-    bias = _c(bias, np.float32)
+    keep, bptr = _bias_ptr(bias)
     N, d = x.shape
     E = w_router.shape[0]
     idx = np.empty((N, k), np.int32)
     w = np.empty((N, k), np.float64)
     flags = np.zeros(N, np.uint8)
     rc = _load().oracle_route(N, d, E, G, TG, k, int(bool(norm_topk_prob)), float(route_scale),
-                              x.ctypes.data, _dtype_code(x), w_router.ctypes.data,
-                              bias.ctypes.data, idx.ctypes.data, w.ctypes.data, flags.ctypes.data)
+                              SCORE_FUNCS[score_func], x.ctypes.data, _dtype_code(x),
+                              w_router.ctypes.data, bptr, idx.ctypes.data, w.ctypes.data,
+                              flags.ctypes.data)
     if rc:
         raise RuntimeError(f"oracle_route failed ({rc})")
     return idx, w, flags
@@ -321,7 +339,8 @@ def combine(out_sorted, inv_perm, topk_weight, residual=None):
     return y
 
 
-def valid_choice(choice_row, G: int, TG: int, k: int, idx, tol: float = 2 * NEAR_TIE_REL) -> bool:
+def valid_choice(choice_row, G: int, TG: int, k: int, idx, tol: float = 2 * NEAR_TIE_REL,
+                 group_by_max: bool = False) -> bool:
     """Is `idx` a legitimate expert choice for this token up to near ties?
 
     It is when some set K of TG groups containing the chosen experts' groups is
@@ -335,7 +354,7 @@ def valid_choice(choice_row, G: int, TG: int, k: int, idx, tol: float = 2 * NEAR
     if len(idx) != k or len(set(idx)) != k or min(idx) < 0 or max(idx) >= E:
         return False
     per = E // G
-    _, _, _, _, gs = select(choice_row, G, TG, k)
+    _, _, _, _, gs = select(choice_row, G, TG, k, group_by_max)
     gs = gs.astype(np.float64)
     groups = sorted({i // per for i in idx})
     if len(groups) > TG:

@@ -74,24 +74,45 @@ static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
 /* [K2-AFF] / [V32-AFF]: logits = linear(x.float(), weight.float()) with no
  * bias term; scores = logits.sigmoid(); the choice scores add the per-expert
  * correction bias. */
+/* [K2-AFF] / [V32-AFF] gate forward: logits = x . W_r^T in fp32 (the fp64 sum
+ * rounded once to fp32); score = sigmoid(logit), or ([V32-AFF]) the softmax of
+ * the token's logits over all experts; choice = score + bias when the router
+ * has a bias, else the score itself.  Each value is rounded to fp32, the
+ * precision the pages compute in. */
 int oracle_router_scores(int64_t N, int64_t d, int64_t E, const void* x, int x_dtype,
-                         const float* w_router, const float* bias, float* logit, float* score,
-                         float* choice) {
-  if (N < 0 || d <= 0 || E <= 0 || !x || !w_router || !bias || !score || !choice) return 1;
-#pragma omp parallel for schedule(static)
+                         const float* w_router, const float* bias, int score_func, float* logit,
+                         float* score, float* choice) {
+  if (N < 0 || d <= 0 || E <= 0 || !x || !w_router || !score || !choice) return 1;
+  if (score_func != ORACLE_SCORE_SIGMOID && score_func != ORACLE_SCORE_SOFTMAX) return 1;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
   for (int64_t n = 0; n < N; ++n) {
+    float* l = (float*)malloc(sizeof(float) * (size_t)E);
+    if (!l) {
+      ++bad;
+      continue;
+    }
     for (int64_t e = 0; e < E; ++e) {
       double acc = 0.0;
       for (int64_t i = 0; i < d; ++i) acc += elem(x, x_dtype, n * d + i) * (double)w_router[e * d + i];
-      const float l = (float)acc;
-      const float s = (float)sigmoid((double)l);
-      const float b = (float)((double)s + (double)bias[e]);
-      if (logit) logit[n * E + e] = l;
+      l[e] = (float)acc;
+    }
+    double mx = -INFINITY, den = 0.0;
+    if (score_func == ORACLE_SCORE_SOFTMAX) {
+      for (int64_t e = 0; e < E; ++e) mx = (double)l[e] > mx ? (double)l[e] : mx;
+      for (int64_t e = 0; e < E; ++e) den += exp((double)l[e] - mx);
+    }
+    for (int64_t e = 0; e < E; ++e) {
+      const float s = score_func == ORACLE_SCORE_SOFTMAX ? (float)(exp((double)l[e] - mx) / den)
+                                                         : (float)sigmoid((double)l[e]);
+      const float b = bias ? (float)((double)s + (double)bias[e]) : s;
+      if (logit) logit[n * E + e] = l[e];
       score[n * E + e] = s;
       choice[n * E + e] = b;
     }
+    free(l);
   }
-  return 0;
+  return bad ? 2 : 0;
 }
 
 /* a beats b: larger value, then lower index. */
@@ -112,12 +133,14 @@ static int cmp_i32(const void* a, const void* b) {
 }
 
 /* [K2-AFF]: groups are consecutive runs of E/G experts; a group's score is the
- * sum of its two largest choice scores (topk(2) then sum); the topk_group
+ * sum of its two largest choice scores (topk(2) then sum) -- or, for a router
+ * without a bias ([V32-AFF]), its largest choice score (amax); the topk_group
  * groups with the largest scores are kept; the top_k largest choice scores
  * among the kept groups' experts are chosen.  [V32-AFF] fills the dropped
  * groups with -inf, so their experts are never chosen. */
-int oracle_select(int64_t E, int G, int TG, int k, const float* choice, int32_t* idx_out,
-                  double* gap_expert, double* gap_group, float* group_score_out) {
+int oracle_select(int64_t E, int G, int TG, int k, int group_by_max, const float* choice,
+                  int32_t* idx_out, double* gap_expert, double* gap_group,
+                  float* group_score_out) {
   if (E <= 0 || E > ORACLE_MAX_E || G <= 0 || E % G != 0 || TG < 1 || TG > G || k < 1) return -1;
   const int64_t per = E / G;
   if (per < 2 || (int64_t)k > (int64_t)TG * per) return -1;
@@ -138,7 +161,7 @@ int oracle_select(int64_t E, int G, int TG, int k, const float* choice, int32_t*
         top2 = v;
       }
     }
-    gs[g] = (float)((double)top1 + (double)top2);
+    gs[g] = group_by_max ? top1 : (float)((double)top1 + (double)top2);
     kept[g] = 0;
     if (group_score_out) group_score_out[g] = gs[g];
   }
@@ -211,8 +234,9 @@ void oracle_weights(int k, int norm_topk_prob, double route_scale, const float* 
 }
 
 int oracle_route(int64_t N, int64_t d, int64_t E, int G, int TG, int k, int norm_topk_prob,
-                 double route_scale, const void* x, int x_dtype, const float* w_router,
-                 const float* bias, int32_t* topk_idx, double* topk_weight, uint8_t* flags) {
+                 double route_scale, int score_func, const void* x, int x_dtype,
+                 const float* w_router, const float* bias, int32_t* topk_idx, double* topk_weight,
+                 uint8_t* flags) {
   if (N < 0 || E <= 0 || E > ORACLE_MAX_E || k < 1) return 1;
   if (N == 0) return 0;
   float* score = (float*)malloc(sizeof(float) * (size_t)(N * E));
@@ -222,12 +246,14 @@ int oracle_route(int64_t N, int64_t d, int64_t E, int G, int TG, int k, int norm
     free(choice);
     return 2;
   }
-  int rc = oracle_router_scores(N, d, E, x, x_dtype, w_router, bias, NULL, score, choice);
+  int rc = oracle_router_scores(N, d, E, x, x_dtype, w_router, bias, score_func, NULL, score,
+                                choice);
   int bad = 0;
   if (rc == 0) {
 #pragma omp parallel for schedule(static) reduction(+ : bad)
     for (int64_t n = 0; n < N; ++n) {
-      const int f = oracle_select(E, G, TG, k, choice + n * E, topk_idx + n * k, NULL, NULL, NULL);
+      const int f = oracle_select(E, G, TG, k, bias == NULL, choice + n * E, topk_idx + n * k,
+                                  NULL, NULL, NULL);
       if (f < 0) {
         ++bad;
         continue;

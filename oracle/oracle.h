@@ -43,17 +43,22 @@ extern "C" {
 
 int oracle_num_threads(void);
 
+#define ORACLE_SCORE_SIGMOID 0
+#define ORACLE_SCORE_SOFTMAX 1
+
 /* Router scores for all tokens, rounded to fp32 as the pages compute them:
- * logit (fp32 linear), score = sigmoid(logit), choice = score + bias. */
+ * logit (fp32 linear), score = sigmoid(logit) or softmax over the experts,
+ * choice = score + bias (bias may be NULL: choice = score). */
 int oracle_router_scores(int64_t N, int64_t d, int64_t E, const void* x, int x_dtype,
-                         const float* w_router, const float* bias, float* logit, float* score,
-                         float* choice);
+                         const float* w_router, const float* bias, int score_func, float* logit,
+                         float* score, float* choice);
 
 /* Group pruning and expert choice for one token from its choice scores:
  * idx_out[k] ascending; gap_expert / gap_group are the relative gaps at the
  * k-th / TG-th boundary (+inf when there is no competitor). Returns flags. */
-int oracle_select(int64_t E, int G, int TG, int k, const float* choice, int32_t* idx_out,
-                  double* gap_expert, double* gap_group, float* group_score_out);
+int oracle_select(int64_t E, int G, int TG, int k, int group_by_max, const float* choice,
+                  int32_t* idx_out, double* gap_expert, double* gap_group,
+                  float* group_score_out);
 
 /* Routing weights for one token from its scores and chosen experts. */
 void oracle_weights(int k, int norm_topk_prob, double route_scale, const float* score,
@@ -61,8 +66,9 @@ void oracle_weights(int k, int norm_topk_prob, double route_scale, const float* 
 
 /* Full router: scores, selection, weights for all N tokens. */
 int oracle_route(int64_t N, int64_t d, int64_t E, int G, int TG, int k, int norm_topk_prob,
-                 double route_scale, const void* x, int x_dtype, const float* w_router,
-                 const float* bias, int32_t* topk_idx, double* topk_weight, uint8_t* flags);
+                 double route_scale, int score_func, const void* x, int x_dtype,
+                 const float* w_router, const float* bias, int32_t* topk_idx, double* topk_weight,
+                 uint8_t* flags);
 
 /* Per-expert counts, offsets and the stable dispatch permutation. */
 int oracle_counts_perm(int64_t N, int k, int64_t E, const int32_t* topk_idx, int32_t* counts,

@@ -38,33 +38,40 @@ def _golden_cases():
 @pytest.mark.parametrize("case,tok", list(_golden_cases()))
 def test_worked_examples(case, tok):
     E = case["E"]
-    w_router = np.array([[logit(p)] for p in case["p"]], np.float32)
-    bias = np.array(case["bias"], np.float32)
+    score_func = case.get("score_func", "sigmoid")
+    if score_func == "softmax":
+        w_router = np.array([[math.log(q)] for q in case["q"]], np.float32)
+    else:
+        w_router = np.array([[logit(p)] for p in case["p"]], np.float32)
+    bias = None if case["bias"] is None else np.array(case["bias"], np.float32)
     x = np.array([[tok["x"]]], np.float32)
     idx, w, flags = oracle.route(x, w_router, bias, case["G"], case["TG"], case["k"],
-                                 case["norm_topk_prob"], case["route_scale"])
+                                 case["norm_topk_prob"], case["route_scale"], score_func)
     assert idx[0].tolist() == tok["idx"]
     np.testing.assert_allclose(w[0], tok["weight"], rtol=1e-6)
     assert bool(flags[0] & oracle.FLAG_NEAR_TIE_EXPERT) == tok["near_tie"]
-    assert E == len(case["p"])
+    assert E == w_router.shape[0]
 
 
 def _random_choice(rng, E, spread=1.0):
     return rng.normal(0.5, spread, E).astype(np.float32)
 
 
+@pytest.mark.parametrize("group_by_max", [False, True])
 @pytest.mark.parametrize("E,G,TG,k", [(8, 4, 2, 3), (12, 3, 2, 4), (16, 4, 2, 4), (16, 8, 3, 5),
                                       (10, 1, 1, 3), (12, 6, 6, 2), (9, 3, 1, 3), (8, 2, 1, 1)])
-def test_brute_force_selection(E, G, TG, k):
-    rng = np.random.default_rng(E * 100 + G * 10 + k)
+def test_brute_force_selection(E, G, TG, k, group_by_max):
+    rng = np.random.default_rng(E * 100 + G * 10 + k + 7 * group_by_max)
     per = E // G
     for _ in range(60):
         b = _random_choice(rng, E)
-        idx, flags, _, _, gs = oracle.select(b, G, TG, k)
-        # group scores: the two largest choice scores of each group, summed in fp32
+        idx, flags, _, _, gs = oracle.select(b, G, TG, k, group_by_max)
+        # group scores: the two largest choice scores of each group summed in
+        # fp32, or (a router without bias) the largest one
         for g in range(G):
             top2 = sorted(b[g * per:(g + 1) * per].tolist(), reverse=True)[:2]
-            assert gs[g] == np.float32(np.float64(top2[0]) + np.float64(top2[1]))
+            want = top2[0] if group_by_max else np.float32(np.float64(top2[0]) + np.float64(top2[1]))
+            assert gs[g] == np.float32(want)
         best_groups = max(itertools.combinations(range(G), TG),
                           key=lambda s: sum(float(gs[g]) for g in s))
         cands = [e for e in range(E) if e // per in best_groups]
@@ -223,3 +230,63 @@ def test_config_rejections():
     for G, TG, k in [(3, 1, 1), (8, 1, 1), (4, 5, 1), (4, 0, 1), (4, 1, 3), (2, 1, 0)]:
         with pytest.raises(ValueError):
             oracle.select(b, G, TG, k)
+
+
+# ---- softmax scoring and routers without a bias (DeepSeek-V3.2-Exp gate) ----
+
+def test_softmax_scores_match_scipy():
+    """Softmax scores: scipy's float64 softmax of the fp32 logits, rounded to
+    fp32; they sum to one; without a bias the choice is the score."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(5)
+    N, d, E = 40, 48, 24
+    x = rng.normal(0, 1, (N, d)).astype(np.float32)
+    wr = rng.normal(0, 1 / math.sqrt(d), (E, d)).astype(np.float32)
+    lg, s, b = oracle.router_scores(x, wr, None, "softmax")
+    ref = softmax(lg.astype(np.float64), axis=1).astype(np.float32)
+    np.testing.assert_allclose(s, ref, rtol=2e-7, atol=0)
+    np.testing.assert_allclose(s.astype(np.float64).sum(axis=1), 1.0, rtol=1e-6)
+    assert np.array_equal(b, s)
+    lg2, s2, b2 = oracle.router_scores(x, wr, None, "sigmoid")
+    assert np.array_equal(lg, lg2) and np.array_equal(b2, s2)
+    bias = rng.normal(0, 0.01, E).astype(np.float32)
+    _, s3, b3 = oracle.router_scores(x, wr, bias, "softmax")
+    assert np.array_equal(s3, s)
+    np.testing.assert_allclose(b3, (s.astype(np.float64) + bias).astype(np.float32), rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("norm", [False, True])
+def test_softmax_zero_token_closed_form(norm):
+    """A zero token: every softmax score is 1/E, so the weights are route_scale/E
+    (route_scale/k after renormalisation) and ties go to the lowest ids."""
+    E, G, TG, k = 16, 4, 2, 3
+    rng = np.random.default_rng(9)
+    wr = rng.normal(0, 1, (E, 8)).astype(np.float32)
+    x = np.zeros((1, 8), np.float32)
+    idx, w, flags = oracle.route(x, wr, None, G, TG, k, norm, 3.0, "softmax")
+    assert idx[0].tolist() == [0, 1, 2]
+    np.testing.assert_allclose(w[0], 3.0 / k if norm else 3.0 / E, rtol=1e-7)
+    assert flags[0] & oracle.FLAG_NEAR_TIE_EXPERT
+
+
+def test_route_without_bias_invariants():
+    """No bias, sigmoid and softmax: the chosen experts are the top-k scores of
+    the groups kept by their largest score, weights are proportional to them."""
+    rng = np.random.default_rng(12)
+    N, d, E, G, TG, k = 64, 32, 32, 8, 3, 4
+    x = rng.normal(0, 1, (N, d)).astype(np.float32)
+    wr = rng.normal(0, 1 / math.sqrt(d), (E, d)).astype(np.float32)
+    per = E // G
+    for sf in ("sigmoid", "softmax"):
+        idx, w, flags = oracle.route(x, wr, None, G, TG, k, True, 2.0, sf)
+        _, s, _ = oracle.router_scores(x, wr, None, sf)
+        for n in range(N):
+            gmax = s[n].reshape(G, per).max(axis=1)
+            kept = set(np.argsort(-gmax, kind="stable")[:TG].tolist())
+            assert all(e // per in kept for e in idx[n])
+            cand = [e for e in range(E) if e // per in kept]
+            top = sorted(cand, key=lambda e: (-s[n, e], e))[:k]
+            if not flags[n]:
+                assert sorted(top) == idx[n].tolist()
+            np.testing.assert_allclose(w[n], 2.0 * s[n, idx[n]] / s[n, idx[n]].astype(np.float64).sum(),
+                                       rtol=1e-6)
