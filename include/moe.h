@@ -59,7 +59,8 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
 /* [K3-GATE]: experts use SiLU (act_fn(w1 x) * w3 x) or SiTU. */
 typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SITU = 1 } moe_act;
 
-/* [V32-AFF] offers softmax scoring; libmoe runs sigmoid only ([K2-AFF]). */
+/* [K2-AFF] scores with the sigmoid of each logit; [V32-AFF] also offers the
+ * softmax of the token's logits over all experts. */
 typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score_func;
 
 /* [K2-AFF] raises for any top-k method other than noaux_tc. */
@@ -84,7 +85,7 @@ typedef struct {
   int32_t top_k;           /* k = num_experts_per_tok, 1 <= k <= min(16, TG * E / G) */
   int32_t norm_topk_prob;  /* renormalise the k weights (applied only when k > 1) */
   float route_scale;       /* routed_scaling_factor */
-  int32_t score_func;      /* moe_score_func: SIGMOID (SOFTMAX -> MOE_ERR_UNSUPPORTED) */
+  int32_t score_func;      /* moe_score_func: SIGMOID or SOFTMAX */
   int32_t topk_method;     /* moe_topk_method: NOAUX_TC */
   int32_t training;        /* must be 0: inference only (training -> UNSUPPORTED) */
   int64_t d_ff;            /* moe_intermediate_size of a routed expert */
@@ -101,7 +102,7 @@ typedef struct {
 /* Weights of one block.  d_in = d_latent if d_latent > 0, else d. */
 typedef struct {
   const float* w_router;  /* [E, d] fp32 router weight ([K2-AFF] gate-init) */
-  const float* bias;      /* [E] fp32 e_score_correction_bias, choice only */
+  const float* bias;      /* [E] fp32 e_score_correction_bias, choice only; NULL: none */
   const void* w1;         /* [E, d_ff, d_in] dtype, gate projections */
   const void* w3;         /* [E, d_ff, d_in] dtype, up projections */
   const void* w2;         /* [E, d_in, d_ff] dtype, down projections */
@@ -125,14 +126,18 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t N, int32_t call, si
 /*
  * moe_route - the router ([K2-AFF] gate-forward; [V32-AFF] gate-forward).
  *   logits = hidden . w_router^T in fp32 (hidden widened exactly), no bias;
- *   score = sigmoid(logits); choice = score + bias (selection only);
+ *   score = sigmoid(logits), or with MOE_SCORE_SOFTMAX the softmax of the
+ *   token's logits over all E experts ([V32-AFF]);
+ *   choice = score + bias (selection only), or score when bias is NULL;
  *   group g = experts [g*E/G, (g+1)*E/G); group score = sum of its two largest
- *   choice values; the TG best groups are kept and the others dropped (their
- *   experts can never be chosen); the k largest choice values among the kept
- *   experts are chosen (ties to the lower index); weight = score of the chosen
- *   expert, divided by (sum of the k scores + 1e-20) when norm_topk_prob and
- *   k > 1, times route_scale.
- * hidden [N, d] dtype; w_router [E, d] fp32; bias [E] fp32.
+ *   choice values, or its largest one when bias is NULL ([V32-AFF]); the TG
+ *   best groups are kept and the others dropped (their experts can never be
+ *   chosen); the k largest choice values among the kept experts are chosen
+ *   (ties to the lower index); weight = score of the chosen expert, divided by
+ *   (sum of the k scores + 1e-20) when norm_topk_prob and k > 1, times
+ *   route_scale.  ([V32-AFF] renormalises sigmoid scores only: set
+ *   norm_topk_prob = 0 with softmax for that gate.)
+ * hidden [N, d] dtype; w_router [E, d] fp32; bias [E] fp32 or NULL.
  * Out: topk_idx [N, k] int32, each row's experts in ascending id;
  *      topk_weight [N, k] fp32, in the same slot order.
  * N = 0 is a valid no-op.

@@ -64,6 +64,8 @@ def make_config(*, d, n_experts, n_group, topk_group, top_k, d_ff, route_scale,
                 score_func=SCORE_SIGMOID, topk_method=TOPK_NOAUX_TC, training=False) -> moe_config:
     if isinstance(act, str):
         act = {"silu": ACT_SILU, "situ": ACT_SITU}[act]
+    if isinstance(score_func, str):
+        score_func = {"sigmoid": SCORE_SIGMOID, "softmax": SCORE_SOFTMAX}[score_func]
     return moe_config(d=d, n_experts=n_experts, n_group=n_group, topk_group=topk_group,
                       top_k=top_k, norm_topk_prob=int(bool(norm_topk_prob)),
                       route_scale=route_scale, score_func=score_func, topk_method=topk_method,

@@ -43,6 +43,11 @@ moe_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+#define OPTIONAL_PTR(p)                                                                    \
+  do {                                                                                     \
+    if ((p) != nullptr && !aligned16(p))                                                   \
+      return fail(MOE_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, #p);           \
+  } while (0)
 #define REQUIRE_PTR(p)                                                                     \
   do {                                                                                     \
     if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);        \
@@ -67,8 +72,8 @@ constexpr int64_t kMaxLatent = 16384;  // row width of the fused combine + RMS n
 moe_status validate(const moe_config* c, const char* fn) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "%s: cfg is NULL", fn);
   if (c->training) return fail(MOE_ERR_UNSUPPORTED, "%s: training mode is not supported", fn);
-  if (c->score_func != MOE_SCORE_SIGMOID)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: scoring function %d is not supported (sigmoid only)", fn,
+  if (c->score_func != MOE_SCORE_SIGMOID && c->score_func != MOE_SCORE_SOFTMAX)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: scoring function %d is not supported", fn,
                 c->score_func);
   if (c->topk_method != MOE_TOPK_NOAUX_TC)
     return fail(MOE_ERR_UNSUPPORTED, "%s: top-k method %d is not supported (noaux_tc only)", fn,
@@ -350,7 +355,9 @@ moe_status run_route(const moe_config* c, int64_t N, const void* hidden, const f
     CHECK_HIP(dense_gemm(c, hidden, N, c->d, w_router, nullptr, E, logits, moe::EPI_STORE, nullptr, s));
   }
   const int parts = is_bf16(c) ? (int)p.router_splits : 1;
-  CHECK_HIP(moe::launch_route_select(logits, parts, N * E, bias, N, E, c->n_group, c->topk_group, c->top_k,
+  CHECK_HIP(moe::launch_route_select(logits, parts, N * E, bias,
+                                     c->score_func == MOE_SCORE_SOFTMAX ? 1 : 0, N, E,
+                                     c->n_group, c->topk_group, c->top_k,
                                      c->norm_topk_prob ? 1 : 0, c->route_scale, idx, wts, s));
   return MOE_OK;
 }
@@ -398,7 +405,7 @@ moe_status moe_route(const moe_config* cfg, int64_t N, const void* hidden, const
   if (N == 0) return ok();
   REQUIRE_PTR(hidden);
   REQUIRE_PTR(w_router);
-  REQUIRE_PTR(bias);
+  OPTIONAL_PTR(bias);  // a router without a bias
   REQUIRE_PTR(topk_idx);
   REQUIRE_PTR(topk_weight);
   const Plan p = make_plan(cfg, N, MOE_CALL_ROUTE);
@@ -522,7 +529,7 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
   REQUIRE_PTR(hidden);
   REQUIRE_PTR(y);
   REQUIRE_PTR(w->w_router);
-  REQUIRE_PTR(w->bias);
+  OPTIONAL_PTR(w->bias);  // a router without a bias
   REQUIRE_PTR(w->w1);
   REQUIRE_PTR(w->w3);
   REQUIRE_PTR(w->w2);

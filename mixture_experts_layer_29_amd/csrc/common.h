@@ -93,7 +93,7 @@ int gemm_f32_rows_per_tile();
 hipError_t launch_router_split(const float* w_router, int64_t E, int64_t d, int64_t dp,
                                bf16_t* w_split, hipStream_t s);
 hipError_t launch_route_select(const float* logits, int n_parts, int64_t part_stride,
-                               const float* bias, int64_t N, int64_t E,
+                               const float* bias, int softmax, int64_t N, int64_t E,
                                int G, int TG, int k, int norm, float scale, int32_t* topk_idx,
                                float* topk_weight, hipStream_t s);
 

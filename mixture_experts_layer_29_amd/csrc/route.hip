@@ -9,11 +9,13 @@
 // laid out as one bf16 matrix [E, 3 * dp] (dp = d rounded up to 64, zero pad),
 // so the dense streaming GEMM computes logits = [x x x] . split^T directly.
 //
-// moe_route_select then takes one token per wave: sigmoid scores, bias added
-// for the choice only, per-group sum of the two largest choice values, the
-// best topk_group groups, the top_k choice values among them by k rounds of a
-// wave-wide arg-max (larger value, then lower index), weights from the
-// unbiased scores, renormalised (+1e-20, when top_k > 1) and scaled.
+// moe_route_select then takes one token per wave: sigmoid scores (or the
+// softmax over the token's experts, DeepSeek-V3.2-Exp gate), bias added for
+// the choice only (a router may have none), per-group sum of the two largest
+// choice values (the largest one when there is no bias), the best topk_group
+// groups, the top_k choice values among them by k rounds of a wave-wide
+// arg-max (larger value, then lower index), weights from the unbiased scores,
+// renormalised (+1e-20, when top_k > 1 and asked for) and scaled.
 #include "common.h"
 
 namespace moe {
@@ -70,7 +72,7 @@ constexpr int kMaxG = 1024;
 template <int P>
 __global__ __launch_bounds__(kThreads) void moe_route_select(
     const float* __restrict__ logits, int n_parts, int64_t part_stride,
-    const float* __restrict__ bias, int64_t N, int E, int G,
+    const float* __restrict__ bias, int softmax, int64_t N, int E, int G,
     int TG, int k, int norm, float scale, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_weight) {
   __shared__ float sh_b[4][kMaxG];   // choice values (group stage only)
@@ -80,6 +82,7 @@ __global__ __launch_bounds__(kThreads) void moe_route_select(
   const bool live = n < N;
 
   float s[P], b[P];
+  float lmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < P; ++i) {
     const int e = i * 64 + lane;
@@ -88,12 +91,35 @@ __global__ __launch_bounds__(kThreads) void moe_route_select(
       // in range order, so the logit does not depend on the launch
       float l = logits[n * E + e];
       for (int q = 1; q < n_parts; ++q) l += logits[q * part_stride + n * E + e];
-      s[i] = 1.0f / (1.0f + expf(-l));
-      b[i] = s[i] + bias[e];
+      s[i] = l;
+      lmax = fmaxf(lmax, l);
     } else {
-      s[i] = 0.0f;
-      b[i] = -INFINITY;
+      s[i] = -INFINITY;
     }
+  }
+  if (softmax) {
+    // softmax over the token's E logits: exp(l - max) / sum, in fp32
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, m, 64));
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      s[i] = (i * 64 + lane < E) ? expf(s[i] - lmax) : 0.0f;
+      sum += s[i];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int i = 0; i < P; ++i) s[i] *= inv;
+  } else {
+#pragma unroll
+    for (int i = 0; i < P; ++i) s[i] = (i * 64 + lane < E) ? 1.0f / (1.0f + expf(-s[i])) : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int e = i * 64 + lane;
+    b[i] = (live && e < E) ? (bias ? s[i] + bias[e] : s[i]) : -INFINITY;
   }
 
   if (G > 1) {
@@ -104,7 +130,8 @@ __global__ __launch_bounds__(kThreads) void moe_route_select(
       if (e < E) sh_b[wave][e] = b[i];
     }
     __syncthreads();
-    // group g: sum of its two largest choice values
+    // group g: sum of its two largest choice values (the largest alone for a
+    // router without a bias)
     for (int g = lane; g < G; g += 64) {
       float t1 = -INFINITY, t2 = -INFINITY;
       for (int e = g * per; e < (g + 1) * per; ++e) {
@@ -116,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void moe_route_select(
           t2 = v;
         }
       }
-      sh_gs[wave][g] = t1 + t2;
+      sh_gs[wave][g] = bias ? t1 + t2 : t1;
     }
     __syncthreads();
     // keep TG groups: TG rounds of arg-max over the group scores; a kept
@@ -215,11 +242,11 @@ __global__ __launch_bounds__(kThreads) void moe_route_select(
 
 template <int P>
 hipError_t launch_select(const float* logits, int n_parts, int64_t part_stride, const float* bias,
-                         int64_t N, int64_t E, int G, int TG, int k, int norm, float scale,
-                         int32_t* idx, float* w, hipStream_t s) {
+                         int softmax, int64_t N, int64_t E, int G, int TG, int k, int norm,
+                         float scale, int32_t* idx, float* w, hipStream_t s) {
   const int64_t grid = (N + 3) / 4;
   moe_route_select<P><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(
-      logits, n_parts, part_stride, bias, N, (int)E, G, TG, k, norm, scale, idx, w);
+      logits, n_parts, part_stride, bias, softmax, N, (int)E, G, TG, k, norm, scale, idx, w);
   return hipGetLastError();
 }
 
@@ -235,14 +262,14 @@ hipError_t launch_router_split(const float* w_router, int64_t E, int64_t d, int6
 }
 
 hipError_t launch_route_select(const float* logits, int n_parts, int64_t part_stride,
-                               const float* bias, int64_t N, int64_t E,
+                               const float* bias, int softmax, int64_t N, int64_t E,
                                int G, int TG, int k, int norm, float scale, int32_t* topk_idx,
                                float* topk_weight, hipStream_t s) {
   if (N == 0) return hipSuccess;
   if (n_parts < 1) return hipErrorInvalidValue;
   const int64_t P = (E + 63) / 64;
 #define MOE_SELECT(PP)                                                                       \
-  return launch_select<PP>(logits, n_parts, part_stride, bias, N, E, G, TG, k, norm, scale, \
+  return launch_select<PP>(logits, n_parts, part_stride, bias, softmax, N, E, G, TG, k, norm, scale, \
                            topk_idx, topk_weight, s)
   if (P <= 1) MOE_SELECT(1);
   if (P <= 2) MOE_SELECT(2);

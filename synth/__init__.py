@@ -67,6 +67,10 @@ class Workload:
     dtype: int = BF16  # hidden, expert, shared and latent weights, outputs
     bias_kind: str = "normal"  # "normal" (std bias_std) | "zipf"
     bias_std: float = 0.01
+    # router form (passed to the library and the oracle; the generator still
+    # draws a bias tensor, which a router without one ignores)
+    score_func: str = "sigmoid"  # "sigmoid" | "softmax"
+    use_bias: bool = True
     B: int = 1
     T: int = 0
     seed: int = 0

@@ -36,7 +36,8 @@ def cfg_of(w: synth.Workload):
                          norm_topk_prob=w.norm_topk_prob, act=w.act, situ_beta=w.situ_beta,
                          situ_linear_beta=w.situ_linear_beta, d_latent=w.L,
                          latent_norm=w.latent_norm, norm_eps=w.norm_eps, d_ff_shared=w.d_sh,
-                         dtype=m.DTYPE_BF16 if w.dtype == synth.BF16 else m.DTYPE_F32)
+                         dtype=m.DTYPE_BF16 if w.dtype == synth.BF16 else m.DTYPE_F32,
+                         score_func=w.score_func)
 
 
 def torch_dtype(w: synth.Workload, name: str):
@@ -82,9 +83,10 @@ def device_inputs(w: synth.Workload, on_device_gen: bool = True) -> dict:
     return out
 
 
-def weights_of(dev: dict):
+def weights_of(dev: dict, w: synth.Workload = None):
     m = moe()
-    return m.Weights(w_router=dev["w_router"], bias=dev["bias"], w1=dev["w1"], w3=dev["w3"],
+    bias = dev["bias"] if (w is None or w.use_bias) else None
+    return m.Weights(w_router=dev["w_router"], bias=bias, w1=dev["w1"], w3=dev["w3"],
                      w2=dev["w2"], w_down=dev.get("w_down"), gamma=dev.get("gamma"),
                      w_up=dev.get("w_up"), sh_w1=dev.get("sh_w1"), sh_w3=dev.get("sh_w3"),
                      sh_w2=dev.get("sh_w2"))
@@ -104,9 +106,11 @@ def resolve_routing(x, w_router, bias, w: synth.Workload, gpu_idx, gpu_wt, wt_rt
     recomputes that token's weights from the GPU's indices.  Weights must match
     to wt_rtol.  Returns (indices, weights, flags, n_resolved) in the oracle's
     terms, to be used downstream (counts, permutation, outputs)."""
+    if not w.use_bias:
+        bias = None
     o_idx, o_w, flags = oracle.route(x, w_router, bias, w.G, w.TG, w.k, w.norm_topk_prob,
-                                     w.route_scale)
-    _, score, choice = oracle.router_scores(x, w_router, bias)
+                                     w.route_scale, w.score_func)
+    _, score, choice = oracle.router_scores(x, w_router, bias, w.score_func)
     gpu_idx = np.asarray(gpu_idx)
     diff = np.flatnonzero(np.any(o_idx != gpu_idx, axis=1))
     near = (flags & (oracle.FLAG_NEAR_TIE_EXPERT | oracle.FLAG_NEAR_TIE_GROUP)) != 0
@@ -116,7 +120,8 @@ def resolve_routing(x, w_router, bias, w: synth.Workload, gpu_idx, gpu_wt, wt_rt
     idx = o_idx.copy()
     wt = o_w.copy()
     for n in diff:
-        assert oracle.valid_choice(choice[n], w.G, w.TG, w.k, gpu_idx[n]), (
+        assert oracle.valid_choice(choice[n], w.G, w.TG, w.k, gpu_idx[n],
+                                   group_by_max=bias is None), (
             f"token {n}: near tie resolved to an invalid choice {gpu_idx[n].tolist()}")
         idx[n] = gpu_idx[n]
         wt[n] = oracle.weights(score[n], gpu_idx[n], w.norm_topk_prob, w.route_scale)
@@ -130,15 +135,28 @@ def rel_l2(got, ref) -> float:
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
-def assert_close_bf16(got, ref, what=""):
-    """The bf16 acceptance bar: relative L2 <= 1e-2 and max |err| <= 5e-2 rms(ref)."""
+def assert_close_bf16(got, ref, what="", output_rounding_slack=False):
+    """The bf16 acceptance bar: relative L2 <= 1e-2 and max |err| <= 5e-2 rms(ref).
+
+    output_rounding_slack: widen each element's max-error bar by half a bf16
+    ulp of that element.  Storing y in bf16 alone moves an element by up to
+    2^-9 of its magnitude (relative), which exceeds 5e-2 rms wherever |y| >
+    12.8 rms: only outputs with such heavy tails need it (softmax routing
+    without renormalisation gives tokens very different weight totals)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     r = rel_l2(got, ref)
     rms = float(np.sqrt(np.mean(ref ** 2)))
-    m = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    err = np.abs(got - ref)
+    m = float(np.max(err)) if got.size else 0.0
     assert r <= 1e-2, f"{what}: relative L2 {r:.3e} > 1e-2"
-    assert m <= 5e-2 * rms, f"{what}: max abs err {m:.3e} > 5e-2 * rms {rms:.3e}"
+    if output_rounding_slack and got.size:
+        half_ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 8)
+        worst = float(np.max(err - half_ulp))
+        assert worst <= 5e-2 * rms, (f"{what}: max (abs err - half ulp) {worst:.3e} > "
+                                     f"5e-2 * rms {rms:.3e}")
+    else:
+        assert m <= 5e-2 * rms, f"{what}: max abs err {m:.3e} > 5e-2 * rms {rms:.3e}"
     return r, m / max(rms, 1e-300)
 
 

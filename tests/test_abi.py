@@ -61,7 +61,7 @@ def good(**kw):
     (dict(n_experts=1, n_group=1, topk_group=1, top_k=1), binding.MOE_ERR_INVALID_ARG),
     (dict(n_experts=2048, n_group=1, topk_group=1), binding.MOE_ERR_UNSUPPORTED),
     (dict(n_experts=64, n_group=1, topk_group=1, top_k=17), binding.MOE_ERR_UNSUPPORTED),
-    (dict(score_func=m.binding.SCORE_SOFTMAX), binding.MOE_ERR_UNSUPPORTED),
+    (dict(score_func=7), binding.MOE_ERR_UNSUPPORTED),
     (dict(topk_method=1), binding.MOE_ERR_UNSUPPORTED),
     (dict(training=True), binding.MOE_ERR_UNSUPPORTED),
     (dict(dtype=7), binding.MOE_ERR_UNSUPPORTED),
@@ -114,7 +114,11 @@ def test_route_argument_errors():
     assert call_route(c, 8, ws=None) == binding.MOE_ERR_WORKSPACE
     assert call_route(c, 8, ws=FAKE + 64) == binding.MOE_ERR_WORKSPACE      # not 256-aligned
     assert call_route(c, 8, ws_bytes=16) == binding.MOE_ERR_WORKSPACE
-    assert call_route(good(score_func=1), 8) == binding.MOE_ERR_UNSUPPORTED
+    assert call_route(good(score_func=7), 8) == binding.MOE_ERR_UNSUPPORTED
+    # the bias may be NULL (a router without one) but not misaligned
+    lib = binding.lib()
+    st = lib.moe_route(ctypes.byref(c), 8, FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == binding.MOE_ERR_INVALID_ARG and "bias" in binding.last_error()
 
 
 def test_block_argument_errors():

@@ -21,7 +21,7 @@ def run_block(w, dev, with_outputs=True):
     wt = torch.empty((w.N, w.k), dtype=torch.float32, device="cuda") if with_outputs else None
     cnt = torch.empty((w.E,), dtype=torch.int32, device="cuda") if with_outputs else None
     ws = m.workspace(cfg, w.N, m.CALL_BLOCK)
-    m.moe_block_forward(cfg, w.N, weights_of(dev), dev["hidden"], y, ws, idx, wt, cnt)
+    m.moe_block_forward(cfg, w.N, weights_of(dev, w), dev["hidden"], y, ws, idx, wt, cnt)
     torch.cuda.synchronize()
     return y, idx, wt, cnt
 
@@ -44,7 +44,11 @@ def check_block(w):
     got = as_f64(to_host(y))
     assert np.all(np.isfinite(got))
     if w.dtype == synth.BF16:
-        return assert_close_bf16(got, y_ref, w.name)
+        # softmax routing without renormalisation: |y| reaches ~14 rms, where
+        # bf16 storage of y alone exceeds the max-error bar (see the helper)
+        return assert_close_bf16(got, y_ref, w.name,
+                                 output_rounding_slack=(w.score_func == "softmax"
+                                                        and not w.norm_topk_prob))
     return assert_close_f32(got, y_ref, w.name)
 
 
@@ -69,6 +73,16 @@ VARIANTS = {
     "one_token": TINY.scaled(N=1, dtype=synth.BF16),
     "decode_like": synth.Workload(name="decode_like", N=32, d=2048, E=384, G=1, TG=1, k=8,
                                   d_ff=256, d_sh=256, route_scale=2.827, seed=9),
+    # DeepSeek-V3.2-Exp gate forms: softmax scoring (no renormalisation) and a
+    # router without a bias (groups scored by their largest choice)
+    "softmax_groups_bf16": synth.Workload(name="softmax_groups_bf16", N=300, d=512, E=64, G=8,
+                                          TG=3, k=6, d_ff=128, route_scale=2.5, seed=11,
+                                          score_func="softmax", norm_topk_prob=False),
+    "nobias_groups_bf16": synth.Workload(name="nobias_groups_bf16", N=300, d=512, E=64, G=8,
+                                         TG=3, k=6, d_ff=128, route_scale=2.5, seed=12,
+                                         use_bias=False),
+    "softmax_nobias_fp32": TINY.scaled(name="softmax_nobias_fp32", score_func="softmax",
+                                       use_bias=False, seed=13),
 }
 
 

@@ -16,14 +16,15 @@ def run_route(w, dev):
     idx = torch.full((w.N, w.k), -7, dtype=torch.int32, device="cuda")
     wt = torch.full((w.N, w.k), -7.0, dtype=torch.float32, device="cuda")
     ws = m.workspace(cfg, w.N, m.CALL_ROUTE)
-    m.moe_route(cfg, w.N, dev["hidden"], dev["w_router"], dev["bias"], idx, wt, ws)
+    m.moe_route(cfg, w.N, dev["hidden"], dev["w_router"], dev["bias"] if w.use_bias else None,
+                idx, wt, ws)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), wt.cpu().numpy()
 
 
 def check(w):
-    print(f"route parity: {w.name} N={w.N} E={w.E} G={w.G} TG={w.TG} k={w.k} dtype={w.dtype}",
-          flush=True)
+    print(f"route parity: {w.name} N={w.N} E={w.E} G={w.G} TG={w.TG} k={w.k} dtype={w.dtype} "
+          f"score={w.score_func} bias={w.use_bias}", flush=True)
     dev = device_inputs(w, on_device_gen=False)
     gi, gw = run_route(w, dev)
     x = to_host(dev["hidden"])
@@ -88,3 +89,18 @@ def test_zero_tokens_is_noop():
     m = moe()
     cfg = cfg_of(w)
     m.moe_route(cfg, 0, None, None, None, None, None, None)
+
+
+# Router forms of the DeepSeek-V3.2-Exp gate: softmax scoring, and routers
+# without a bias (groups scored by their largest choice).
+FORMS = [("softmax", True), ("sigmoid", False), ("softmax", False)]
+
+
+@pytest.mark.parametrize("score_func,use_bias", FORMS)
+@pytest.mark.parametrize("N,d,E,G,TG,k,bstd", [SWEEP[0], SWEEP[2], SWEEP[3], SWEEP[4], SWEEP[6],
+                                                SWEEP[7], SWEEP[8]])
+def test_router_forms(N, d, E, G, TG, k, bstd, score_func, use_bias):
+    w = synth.Workload(name="form", N=N, d=d, E=E, G=G, TG=TG, k=k, d_ff=64, route_scale=1.7,
+                       dtype=synth.BF16, bias_std=bstd, seed=N + E + 1, score_func=score_func,
+                       use_bias=use_bias, norm_topk_prob=(score_func == "sigmoid"))
+    check(w)

@@ -35,7 +35,7 @@ def test_full_workload(name):
     wt = torch.empty((w.N, w.k), dtype=torch.float32, device="cuda")
     cnt = torch.empty((w.E,), dtype=torch.int32, device="cuda")
     ws = m.workspace(cfg, w.N, m.CALL_BLOCK)
-    m.moe_block_forward(cfg, w.N, weights_of(dev), dev["hidden"], y, ws, idx, wt, cnt)
+    m.moe_block_forward(cfg, w.N, weights_of(dev, w), dev["hidden"], y, ws, idx, wt, cnt)
     torch.cuda.synchronize()
 
     # routing on every token, against host copies from the host generator
