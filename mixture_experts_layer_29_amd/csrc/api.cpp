@@ -215,7 +215,7 @@ Plan make_plan(const moe_config* c, int64_t N, int call) {
     p.base = cv.take((size_t)p.n_chunks * E * 4);
   }
   if (call == MOE_CALL_GATE_UP || call == MOE_CALL_DOWN || block) {
-    p.mt_off = cv.take((size_t)(E + 1) * 4);
+    p.mt_off = cv.take((size_t)(E + 1 + 9) * 4);  // m-tile prefix, then the XCD split
     p.tile_seg = cv.take((size_t)p.tile_cap * 4);
   }
   if (block) {

@@ -66,7 +66,8 @@ struct GemmArgs {
   int64_t k_splits;       // dense only: K is cut into this many ranges (0 or 1: none),
   int64_t k_split_blocks; //   each of this many 64-wide blocks, every range non-empty;
   int64_t c_split_stride; //   range s writes its partial product at C + s * c_split_stride
-  const int32_t* mt_off;  // [S+1] m-tile prefix (grouped only)
+  const int32_t* mt_off;  // [S+1] m-tile prefix, then [9] first segment of each XCD's run
+                          // (grouped only)
   int64_t n_seg;          // S, segments (grouped only)
   const int32_t* tile_seg;// m-tile -> segment, -1 past the last (grouped only)
   int64_t tile_cap;       // entries of tile_seg

@@ -437,9 +437,11 @@ template <int RB, int EPI, int AMODE, bool KT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void moe_gemm_bf16(GemmArgs a, int64_t n_tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<RB>::kBytes];
+  int64_t L, end, step;
+  gemm::tile_range<RB * 32>(a, blockIdx.x, gridDim.x, n_tiles_n, L, end, step);
+  for (; L < end; L += step) {
   TileLoc t;
-  const int64_t L = gemm::tile_of_block<RB * 32>(a, blockIdx.x, n_tiles_n);
-  if (L < 0 || !gemm::locate<RB * 32>(a, L, n_tiles_n, t)) return;
+  if (!gemm::locate<RB * 32>(a, L, n_tiles_n, t)) continue;
   const int nrb = (t.rows + 31) >> 5;
   switch (nrb) {
     case 1: gemm_tile<1, RB, EPI, AMODE, KT>(a, t, smem); break;
@@ -450,6 +452,7 @@ void moe_gemm_bf16(GemmArgs a, int64_t n_tiles_n) {
     case 6: if constexpr (RB >= 6) gemm_tile<6, RB, EPI, AMODE, KT>(a, t, smem); break;
     case 7: if constexpr (RB >= 7) gemm_tile<7, RB, EPI, AMODE, KT>(a, t, smem); break;
     default: if constexpr (RB >= 8) gemm_tile<8, RB, EPI, AMODE, KT>(a, t, smem); break;
+  }
   }
 }
 

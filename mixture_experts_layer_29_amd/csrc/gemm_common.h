@@ -7,23 +7,32 @@
 namespace moe {
 namespace gemm {
 
-// Work-groups are dispatched to the 8 XCDs round-robin (id % 8).  The grid of a
-// grouped product is sized for the most m-tiles the routing can produce, while
-// the tiles that exist (T, known on the device only) are numbered from 0; so
-// the T tiles are split into 8 contiguous runs of ceil(T/8), and work-group id
-// takes tile (id % 8) * ceil(T/8) + id / 8: every XCD gets an equal, contiguous
-// share (consecutive tiles share weights or activations in its L2).  Returns
-// -1 for a work-group with no tile.  The grid holds at least 8 * ceil(T/8).
+// Work-groups are dispatched to the 8 XCDs round-robin (id % 8); work-group id
+// runs as the (id / 8)-th of its XCD's grid / 8 work-groups.  Grouped
+// products: the dispatch scan split the segments into 8 runs of about equal
+// estimated cost (mt_off[S+1 .. S+9]), and XCD x takes the tiles of its run
+// (contiguous: the tiles of one expert share its activation rows in the XCD's
+// L2), its work-groups striding through them.  Dense products: the T tiles
+// are cut into 8 contiguous runs of ceil(T/8).  A work-group processes tiles
+// first, first + step, ... below end.
 template <int BM>
-__device__ __forceinline__ int64_t tile_of_block(const GemmArgs& a, int64_t bid, int64_t n_tiles_n) {
-  const int64_t T = a.seg_off ? (int64_t)a.mt_off[a.n_seg] * n_tiles_n
-                              : (a.dense_rows + BM - 1) / BM * n_tiles_n *
-                                    (a.k_splits > 1 ? a.k_splits : 1);
+__device__ __forceinline__ void tile_range(const GemmArgs& a, int64_t bid, int64_t nwg,
+                                           int64_t n_tiles_n, int64_t& first, int64_t& end,
+                                           int64_t& step) {
+  const int64_t x = bid & 7, i = bid >> 3;
+  step = nwg >> 3;
+  if (a.seg_off) {
+    const int32_t* xs = a.mt_off + a.n_seg + 1;
+    first = (int64_t)a.mt_off[xs[x]] * n_tiles_n + i;
+    end = (int64_t)a.mt_off[xs[x + 1]] * n_tiles_n;
+    return;
+  }
+  const int64_t T = (a.dense_rows + BM - 1) / BM * n_tiles_n * (a.k_splits > 1 ? a.k_splits : 1);
   const int64_t per = (T + 7) >> 3;
-  const int64_t i = bid >> 3;
-  if (i >= per) return -1;
-  const int64_t L = (bid & 7) * per + i;
-  return L < T ? L : -1;
+  first = x * per + i;
+  end = min(T, (x + 1) * per);
+  step = i < per ? per : 1;  // one tile each (the grid holds 8 * per work-groups)
+  if (i >= per) first = end;
 }
 
 // Expert activations (Kimi K3 "Gate features" page: expert and situ excerpts):

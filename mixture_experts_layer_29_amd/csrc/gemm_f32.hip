@@ -18,9 +18,11 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_f32(GemmArgs a, int64_t n_t
   __shared__ float As[16][kRows + 1];
   __shared__ float Bs[2][16][64 + 1];
   const int tid = threadIdx.x;
+  int64_t L, end, step;
+  gemm::tile_range<kRows>(a, blockIdx.x, gridDim.x, n_tiles_n, L, end, step);
+  for (; L < end; L += step) {
   TileLoc t;
-  const int64_t L = gemm::tile_of_block<kRows>(a, blockIdx.x, n_tiles_n);
-  if (L < 0 || !gemm::locate<kRows>(a, L, n_tiles_n, t)) return;
+  if (!gemm::locate<kRows>(a, L, n_tiles_n, t)) continue;
   const int64_t K = a.K;
   const int tx = tid & 15, ty = tid >> 4;
   const int64_t col0 = t.j * 64;
@@ -90,6 +92,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_f32(GemmArgs a, int64_t n_t
       if (EPI == EPI_STORE_RES) v += static_cast<const float*>(a.residual)[orow * a.ld_res + col];
       static_cast<float*>(a.C)[orow * a.ldc + col] = v;
     }
+  }
   }
 }
 

@@ -57,6 +57,32 @@ __device__ int32_t block_exclusive_scan(int32_t v, int32_t* sh, int32_t* total) 
   return incl - v;
 }
 
+// Splits the segments (in id order, so each XCD gets a contiguous run) into 8
+// runs of about equal estimated cost, one per XCD, and writes the run
+// boundaries xcd_seg[0..8] (xcd_seg[0] = 0; xcd_seg[x] for x = 1..7 is the
+// first segment whose cost-prefix reaches x/8 of the total, E if none).  A
+// segment's cost: kTileCost per m-tile (streaming its weights) plus one per
+// 32-row block (its MFMA work).  Thread e owns segment e; every thread calls.
+constexpr int32_t kTileCost = 4;
+__device__ void xcd_split(int64_t E, int32_t cnt, int32_t mt, int32_t* sh,
+                          int32_t* __restrict__ xcd_seg) {
+  const int e = threadIdx.x;
+  const int32_t cost = e < E ? mt * kTileCost + (cnt + 31) / 32 : 0;
+  int32_t total;
+  block_exclusive_scan(cost, sh, &total);  // leaves the inclusive prefix in sh
+  if (e < 9) xcd_seg[e] = e == 0 ? 0 : (int32_t)E;
+  __syncthreads();
+  if (e < E) {
+    const int64_t start = e == 0 ? 0 : sh[e - 1];
+    const int64_t prev_start = e >= 2 ? sh[e - 2] : 0;
+    for (int x = 1; x < 8; ++x) {
+      const int64_t mark = ((int64_t)total * x + 7) / 8;
+      if (start >= mark && (e == 0 || prev_start < mark)) xcd_seg[x] = e;
+    }
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kScanThreads) void moe_dispatch_scan(
     const uint64_t* __restrict__ bits, int64_t n_chunks, int64_t E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ base, int rows_per_tile,
@@ -108,6 +134,7 @@ __global__ __launch_bounds__(kScanThreads) void moe_dispatch_scan(
     }
     if (e == 0) mt_off[E] = mt_total;
     for (int64_t u = (int64_t)mt_total + e; u < tile_cap; u += kScanThreads) tile_seg[u] = -1;
+    xcd_split(E, cnt, mt, sh, mt_off + E + 1);
   }
 }
 
@@ -164,6 +191,7 @@ __global__ __launch_bounds__(kScanThreads) void moe_tiles_from_offsets(
   }
   if (e == 0) mt_off[E] = mt_total;
   for (int64_t u = (int64_t)mt_total + e; u < tile_cap; u += kScanThreads) tile_seg[u] = -1;
+  xcd_split(E, cnt, mt, sh, mt_off + E + 1);
 }
 
 }  // namespace
