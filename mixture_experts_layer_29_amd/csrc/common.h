@@ -81,10 +81,11 @@ struct GemmArgs {
   float lbeta;            // SiTU linear beta (<= 0: none)
 };
 
-// bf16 MFMA streaming GEMM; rb = row blocks of 32 per work-group (1, 2, 4);
+// bf16 MFMA streaming GEMM; rb = row blocks of 32 per work-group (1, 2, 4, 6,
+// 8), waves = 4 or 8 per work-group (8: rb 4 and 8 only, two per SIMD);
 // grid capacity `mt_cap` m-tiles (grouped) is an upper bound of mt_off[S].
-hipError_t launch_gemm_bf16(const GemmArgs& a, int epi, int amode, int rb, int64_t mt_cap,
-                            hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmArgs& a, int epi, int amode, int rb, int waves,
+                            int64_t mt_cap, hipStream_t s);
 // fp32 SIMT GEMM for fp32 blocks (64-row m-tiles).
 hipError_t launch_gemm_f32(const GemmArgs& a, int epi, int amode, int64_t mt_cap, hipStream_t s);
 int gemm_f32_rows_per_tile();

@@ -47,6 +47,8 @@
 // Inside a 64-wide K block the lanes visit K in an order of our choosing, the
 // same for both operands (lane half h takes elements 32h .. 32h+31, eight per
 // MFMA step).
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace moe {
@@ -73,27 +75,31 @@ __device__ __forceinline__ void dma16(const void* src, const uint8_t* lds) {
   }
 }
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kPairs = 4;                           // column pairs (32+32 columns) per tile
 constexpr int kRowBytes = 128;                      // one 64-element K block of a bf16 row
-constexpr int kBRows = 32;                          // weight rows per wave per sub-block
-constexpr int kBLoads = kBRows / 8;                 // loads per wave per sub-block: 4
-constexpr int kBWave = kBRows * kRowBytes;          // 4 KB
-constexpr int kBStage = kWaves * kBWave;            // 16 KB
+constexpr int kBRows = 32;                          // weight rows of a column pair per sub-block
+constexpr int kBPair = kBRows * kRowBytes;          // 4 KB
+constexpr int kBStage = kPairs * kBPair;            // 16 KB
 constexpr int kLdsMax = 160 * 1024;                 // LDS of one CU
 constexpr int kLdsOut = 72;                         // fp32 per LDS epilogue row: 64 + 8 pad
-constexpr int kEpiBytes = kWaves * 32 * kLdsOut * 4;
 
+// Waves per work-group, W: 4 (one per column pair and SIMD), or, for tiles of
+// 4 or more row blocks, 8 (two per column pair and SIMD, splitting the row
+// blocks), so that one wave's LDS reads run while the other's MFMAs do: a
+// single wave cannot feed its MFMAs from LDS (~1 KB per 34 cycles per wave on
+// gfx950).  Eight waves pay off when the tiles are mostly full.
+//
 // LDS plan of an RB-block tile: two activation stages, then as many weight
-// stages as fit (at most 9).
-template <int RB>
+// stages as fit (at most 9); the epilogue reuses the start of it.
+template <int RB, int W = 4>
 struct Smem {
   static constexpr int kATile = RB * 32 * kRowBytes;
   static constexpr int kA = 2 * kATile;
   static constexpr int kFit = (kLdsMax - kA) / kBStage;
   static constexpr int kSB = kFit > 9 ? 9 : kFit;
   static constexpr int kB = kSB * kBStage;
-  static constexpr int kBytes = (kA + kB) > kEpiBytes ? (kA + kB) : kEpiBytes;
+  static constexpr int kEpi = W * 32 * kLdsOut * 4;
+  static constexpr int kBytes = (kA + kB) > kEpi ? (kA + kB) : kEpi;
   static_assert(kBytes <= kLdsMax, "LDS plan exceeds one CU");
 };
 
@@ -131,35 +137,48 @@ __device__ __forceinline__ void wg_barrier() {
 }
 
 // NR: 32-row blocks holding rows.  The weight ring has SB = Smem<RB>::kSB
-// stages of one column sub-block each.
-template <int NR, int RB, int EPI, int AMODE, bool KT>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, uint8_t* smem) {
+// stages of one column sub-block each.  W waves; this wave serves column pair
+// cw and, of the tile's NR row blocks, the NRH starting at block rb0 (all of
+// them when W = 4; with W = 8 the waves h = 0 and h = 1 of a pair take the
+// first ceil(NR/2) and the last floor(NR/2)).  It also loads NRH of the
+// tile's 4 NR activation loads (8 rows each) and 4 * 4 / (W / 4) of its
+// column pair's weight loads per sub-block.
+template <int NR, int NRH, int W, int RB, int EPI, int AMODE, bool KT>
+__device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, uint8_t* smem,
+                                          const int cw, const int h) {
   constexpr int SB = Smem<RB>::kSB;
+  constexpr int kBL = W == 8 ? 2 : 4;      // weight loads per wave per sub-block
+  constexpr int NRA = NRH > 0 ? NRH : 1;   // array extents
+  constexpr int C0 = W == 8 ? (NR + 1) / 2 : NR;  // row blocks of the h = 0 wave
   static_assert(SB >= 4, "the wait counts assume weights at least three sub-blocks ahead");
   constexpr int CPW = (EPI == EPI_GATE_UP) ? 32 : 64;  // output columns per wave
   constexpr int ATILE = Smem<RB>::kATile;
   uint8_t* const As = smem;                            // [2][RB*32 rows][128 B]
-  uint8_t* const Bs = smem + Smem<RB>::kA;             // [SB][wave][32 rows][128 B]
+  uint8_t* const Bs = smem + Smem<RB>::kA;             // [SB][pair][32 rows][128 B]
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int rb0 = h ? C0 : 0;                          // first row block of this wave
+  const int a_base = h ? kPairs * C0 + cw * NRH : cw * NRH;  // first activation load
   const int64_t K = a.K;                // row length of both operands
   const int64_t kbase = t.kb0;          // the tile's K range: blocks kbase .. kbase+nkb-1
   const int64_t nkb = t.kb1 - t.kb0;
   const int slot = lane & 7;  // LDS chunk slot this lane's load lands in
 
   // ---- weights: sub-block (kb, c) holds the 32 rows of column block c of the
-  // wave (c = 0: columns cb0.., c = 1: columns cb1..); load i fills rows 8i..8i+7
-  const int64_t cb0 = t.j * (kWaves * CPW) + (int64_t)wave * CPW;
+  // pair (c = 0: columns cb0.., c = 1: columns cb1..); load ib fills rows
+  // 8 ib .. 8 ib + 7, this wave issuing loads ib = b_base .. b_base + kBL - 1
+  const int b_base = W == 8 ? 2 * h : 0;
+  const int64_t cb0 = t.j * (kPairs * CPW) + (int64_t)cw * CPW;
   const int64_t cb1 = (EPI == EPI_GATE_UP) ? cb0 : cb0 + 32;
   const bf16_t* W0 = static_cast<const bf16_t*>(a.B0) + t.seg * a.b_seg_stride;
   const bf16_t* W1 =
       static_cast<const bf16_t*>(EPI == EPI_GATE_UP ? a.B1 : a.B0) + t.seg * a.b_seg_stride;
-  const bf16_t* brow[2][kBLoads];  // this lane's source (row, chunk) per column block and load
-  int bchunk[kBLoads];
+  const bf16_t* brow[2][kBL];  // this lane's source (row, chunk) per column block and load
+  int bchunk[kBL];
 #pragma unroll
-  for (int i = 0; i < kBLoads; ++i) {
-    const int r = 8 * i + (lane >> 3);
+  for (int i = 0; i < kBL; ++i) {
+    const int r = 8 * (b_base + i) + (lane >> 3);
     bchunk[i] = slot ^ ((r >> 1) & 7);
     // columns past the end reload the last column (their outputs are dropped)
     const int64_t c0 = min(cb0 + r, a.n_cols - 1);
@@ -168,12 +187,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
     brow[1][i] = W1 + c1 * K + bchunk[i] * 8;
   }
 
-  // ---- activations: wave w fills tile rows 8(w*NR + i) .. +7 with load i
-  const bf16_t* ap[NR];
-  int achunk[NR];
+  // ---- activations: this wave's load i fills tile rows 8(a_base + i) .. +7
+  const bf16_t* ap[NRA];
+  int achunk[NRA];
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int row = 8 * (wave * NR + i) + (lane >> 3);
+  for (int i = 0; i < NRH; ++i) {
+    const int row = 8 * (a_base + i) + (lane >> 3);
     achunk[i] = slot ^ ((row >> 1) & 7);
     int64_t src = t.row0 + (row < t.rows ? row : 0);
     if (AMODE == A_GATHER) src = a.a_map[src] / a.a_div;
@@ -188,9 +207,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
   auto issue_a = [&](int64_t kb, int stage) {
     kb = kbase + (kb < 0 ? 0 : (kb >= nkb ? nkb - 1 : kb));
     const int64_t col = (AMODE == A_REPEAT ? (kb % a_per_blocks) : kb) * 64;
-    uint8_t* const dst = As + stage * ATILE + wave * NR * 1024;
+    uint8_t* const dst = As + stage * ATILE + a_base * 1024;
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
+    for (int i = 0; i < NRH; ++i) {
       int64_t c = col;
       // past the valid width: A_REPEAT meets zero weights, the K tail is zeroed
       // in LDS after the copy; either way the address stays inside the row
@@ -204,9 +223,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
   const bool b_nt = a.b_stream != 0;
   auto issue_b = [&](int64_t kb, int cblk, int stage) {
     kb = kbase + (kb >= nkb ? nkb - 1 : kb);
-    uint8_t* const dst = Bs + stage * kBStage + wave * kBWave;
+    uint8_t* const dst = Bs + stage * kBStage + cw * kBPair + b_base * 1024;
 #pragma unroll
-    for (int i = 0; i < kBLoads; ++i) {
+    for (int i = 0; i < kBL; ++i) {
       int64_t off = kb * 64;
       if (KT) off = min(off, K - 8 - bchunk[i] * 8);  // A is zero there
       if (b_nt) {
@@ -218,18 +237,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
   };
   // K tail: zero this lane's activation chunks of the last block that lie past K
   auto zero_a_tail = [&](int64_t kb, int stage) {
-    uint8_t* const dst = As + stage * ATILE + wave * NR * 1024;
+    uint8_t* const dst = As + stage * ATILE + a_base * 1024;
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
+    for (int i = 0; i < NRH; ++i) {
       if ((kbase + kb) * 64 + achunk[i] * 8 >= K)
         *reinterpret_cast<u32x4*>(dst + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
     }
     wait_lgkm0();
   };
 
-  f32x16 acc[NR][2];
+  f32x16 acc[NRA][2];
 #pragma unroll
-  for (int rb = 0; rb < NR; ++rb) {
+  for (int rb = 0; rb < NRA; ++rb) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -245,16 +264,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
   // every few dozen cycles).
   const int rsel = lane & 31;
   const int cbase = (lane >> 5) * 4;
-  bf16x8 afk[4][NR];  // activation fragments of the current K block
-  auto compute0 = [&](const uint8_t* at, const uint8_t* bt) {
+  // With W = 4 the activation fragments of a K block stay in registers for its
+  // second sub-block; with W = 8 (half the registers) they are read again.
+  constexpr bool kKeepA = W == 4;
+  bf16x8 afk[kKeepA ? 4 : 2][NRA];  // activation fragments (all steps, or two)
+  auto compute0 = [&](auto col_tag, const uint8_t* at, const uint8_t* bt) {
+    constexpr int COL = decltype(col_tag)::value;
     bf16x8 bf[2];
     // weights first: MFMA rb then waits only for the reads up to A row block rb
     auto read_frags = [&](int s, bf16x8& fb) {
       const int c = cbase + s;
       fb = *reinterpret_cast<const bf16x8*>(bt + swz(rsel, c));
 #pragma unroll
-      for (int rb = 0; rb < NR; ++rb) {
-        afk[s][rb] = *reinterpret_cast<const bf16x8*>(at + swz(rb * 32 + rsel, c));
+      for (int rb = 0; rb < NRH; ++rb) {
+        afk[kKeepA ? s : (s & 1)][rb] =
+            *reinterpret_cast<const bf16x8*>(at + swz((rb0 + rb) * 32 + rsel, c));
       }
     };
     read_frags(0, bf[0]);
@@ -263,13 +287,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
     for (int s = 0; s < 4; ++s) {
       if (s < 3) read_frags(s + 1, bf[(s + 1) & 1]);
 #pragma unroll
-      for (int rb = 0; rb < NR; ++rb) {
-        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afk[s][rb], bf[s & 1], acc[rb][0], 0, 0, 0);
+      for (int rb = 0; rb < NRH; ++rb) {
+        acc[rb][COL] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afk[kKeepA ? s : (s & 1)][rb],
+                                                               bf[s & 1], acc[rb][COL], 0, 0, 0);
       }
       if (s < 3) {
         // MFMA, read, MFMA, read, ...: the reads hide under the MFMAs
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
+        for (int i = 0; i < NRH; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
@@ -278,40 +303,58 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto compute1 = [&](const uint8_t* bt) {
-    bf16x8 bf[4];
+  auto compute1 = [&](const uint8_t* at, const uint8_t* bt) {
+    if constexpr (!kKeepA) {
+      compute0(std::integral_constant<int, 1>{}, at, bt);
+    } else {
+      bf16x8 bf[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) bf[s] = *reinterpret_cast<const bf16x8*>(bt + swz(rsel, cbase + s));
-    __builtin_amdgcn_sched_barrier(0);
+      for (int s = 0; s < 4; ++s) bf[s] = *reinterpret_cast<const bf16x8*>(bt + swz(rsel, cbase + s));
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < 4; ++s) {
 #pragma unroll
-      for (int rb = 0; rb < NR; ++rb) {
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afk[s][rb], bf[s], acc[rb][1], 0, 0, 0);
+        for (int rb = 0; rb < NRH; ++rb) {
+          acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afk[s][rb], bf[s], acc[rb][1], 0, 0, 0);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
 
   // ---- pipeline over sub-iterations u = 2 kb + c.  Sub-iteration u first
   // issues sub-block u + SB - 1 into stage (u - 1) % SB, then waits for its
   // own data; for even u it then passes a work-group barrier and issues
-  // A(kb + 1) into A stage (kb+1)&1.  A wave reads only its own slice of a
-  // weight stage, so its own program order protects the slice it refills (its
-  // reads of sub-block u - 1 are done); the activation tile is shared, so the
-  // barrier comes first (every wave's part of A(kb) has landed, and every wave
-  // has read A(kb-1), which its first sub-block keeps in registers).  The same
-  // issues happen for u = 1-SB .. -1 before the loop (the prologue; A blocks
-  // below 0 fetch A(0) again).
+  // A(kb + 1) into A stage (kb+1)&1.  With W = 4 a wave alone reads its
+  // pair's slice of a weight stage, so its own program order protects the
+  // slice it refills (its reads of sub-block u - 1 are done); with W = 8 two
+  // waves share a slice and odd u has a barrier too.  The activation tile is
+  // shared, so the barrier of even u comes first (every wave's part of A(kb)
+  // has landed, and every wave has read A(kb-1), which its first sub-block
+  // keeps in registers).  The same issues happen for u = 1-SB .. -1 before the
+  // loop (the prologue; A blocks below 0 fetch A(0) again).  Per wave:
   //  - even u needs A(kb) (issued at u-2, after that sub-iteration's weights)
   //    and sub-block u (issued at u-SB+1 <= u-3, hence older): younger than
-  //    A(kb) are the weight loads of u-1 and u, 2 kBLoads;
+  //    A(kb) are the weight loads of u-1 and u, 2 kBL (a wave without
+  //    activation loads waits a little longer than it needs);
   //  - odd u needs sub-block u: younger are the A loads of u-SB+1 (when even),
-  //    and all loads of u-SB+2 .. u: kBLoads (SB-1) plus NR at each of the
+  //    and all loads of u-SB+2 .. u: kBL (SB-1) plus NRH at each of the
   //    floor(SB/2) even sub-iterations among u-SB+1 .. u-1.
-  constexpr int kWaitEven = 2 * kBLoads;
-  constexpr int kWaitOdd = kBLoads * (SB - 1) + NR * (SB / 2);
+  constexpr int kWaitEven = 2 * kBL;
+  constexpr int kWaitOdd = kBL * (SB - 1) + NRH * (SB / 2);
   static_assert(kWaitOdd < 64, "vmcnt range");
+  // W = 8 keeps the order wait, barrier, issue in every sub-iteration (one
+  // barrier both publishes the sub-block and frees the stage it refills), so
+  // at a wait nothing of the current sub-iteration is issued yet:
+  //  - even u needs A(kb), the last load of u-2 (after its weights), and
+  //    sub-block u (issued at u-SB+1 <= u-3): younger are the weight loads of
+  //    u-1 only, kBL;
+  //  - odd u needs sub-block u, the first load of u-SB+1: younger are the A
+  //    loads of u-SB+1 (when even) and all loads of u-SB+2 .. u-1: kBL (SB-2)
+  //    plus NRH at each of the floor(SB/2) even sub-iterations among
+  //    u-SB+1 .. u-1.
+  constexpr int kWaitEven8 = kBL;
+  constexpr int kWaitOdd8 = kBL * (SB - 2) + NRH * (SB / 2);
 #pragma unroll
   for (int q = 0; q < SB - 1; ++q) {
     // u = q - (SB-1): sub-block u + SB - 1 = q, then for even u A(u/2 + 1),
@@ -321,51 +364,76 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
   }
 
   int sb = 0;  // stage of the sub-block being consumed
-  const uint8_t* const bt0 = Bs + wave * kBWave;
+  const uint8_t* const bt0 = Bs + cw * kBPair;
   for (int64_t kb = 0; kb < nkb; ++kb) {
     const int sa = (int)(kb & 1);
-    // c = 0
-    {
-      const int64_t ub = 2 * kb + SB - 1;
-      issue_b(ub >> 1, (SB - 1) & 1, sb == 0 ? SB - 1 : sb - 1);
+    if constexpr (W == 4) {
+      // c = 0
+      {
+        const int64_t ub = 2 * kb + SB - 1;
+        issue_b(ub >> 1, (SB - 1) & 1, sb == 0 ? SB - 1 : sb - 1);
+      }
+      wait_vm<kWaitEven>();
+      if (KT && AMODE != A_REPEAT && kb == nkb - 1) zero_a_tail(kb, sa);
+      wg_barrier();
+      issue_a(kb + 1, sa ^ 1);
+      compute0(std::integral_constant<int, 0>{}, As + sa * ATILE, bt0 + sb * kBStage);
+      sb = (sb + 1 == SB) ? 0 : sb + 1;
+      // c = 1: no barrier (the wave's own weight slice, A in registers)
+      {
+        const int64_t ub = 2 * kb + SB;
+        issue_b(ub >> 1, SB & 1, sb == 0 ? SB - 1 : sb - 1);
+      }
+      wait_vm<kWaitOdd>();
+      compute1(As + sa * ATILE, bt0 + sb * kBStage);
+      sb = (sb + 1 == SB) ? 0 : sb + 1;
+    } else {
+      // c = 0
+      wait_vm<kWaitEven8>();
+      if (KT && AMODE != A_REPEAT && kb == nkb - 1) zero_a_tail(kb, sa);
+      wg_barrier();
+      {
+        const int64_t ub = 2 * kb + SB - 1;
+        issue_b(ub >> 1, (SB - 1) & 1, sb == 0 ? SB - 1 : sb - 1);
+      }
+      issue_a(kb + 1, sa ^ 1);
+      compute0(std::integral_constant<int, 0>{}, As + sa * ATILE, bt0 + sb * kBStage);
+      sb = (sb + 1 == SB) ? 0 : sb + 1;
+      // c = 1
+      wait_vm<kWaitOdd8>();
+      wg_barrier();
+      {
+        const int64_t ub = 2 * kb + SB;
+        issue_b(ub >> 1, SB & 1, sb == 0 ? SB - 1 : sb - 1);
+      }
+      compute1(As + sa * ATILE, bt0 + sb * kBStage);
+      sb = (sb + 1 == SB) ? 0 : sb + 1;
     }
-    wait_vm<kWaitEven>();
-    if (KT && AMODE != A_REPEAT && kb == nkb - 1) zero_a_tail(kb, sa);
-    wg_barrier();
-    issue_a(kb + 1, sa ^ 1);
-    compute0(As + sa * ATILE, bt0 + sb * kBStage);
-    sb = (sb + 1 == SB) ? 0 : sb + 1;
-    // c = 1: no barrier (the wave's own weight slice, A in registers)
-    {
-      const int64_t ub = 2 * kb + SB;
-      issue_b(ub >> 1, SB & 1, sb == 0 ? SB - 1 : sb - 1);
-    }
-    wait_vm<kWaitOdd>();
-    compute1(bt0 + sb * kBStage);
-    sb = (sb + 1 == SB) ? 0 : sb + 1;
   }
   wait_vm<0>();
   __syncthreads();
 
-  // ---- epilogue: through LDS as fp32, 16-byte row-contiguous stores.
+  // ---- epilogue: through LDS as fp32 (each wave its own 32 x 72 region, so
+  // its writes and reads are ordered by the wave itself), 16-byte
+  // row-contiguous stores.
   // MFMA layout: lane holds column lane&31, rows 8*(r/4) + 4*(lane/32) + r%4.
   float(*S)[32][kLdsOut] = reinterpret_cast<float(*)[32][kLdsOut]>(smem);
 #pragma unroll
-  for (int rb = 0; rb < NR; ++rb) {
+  for (int rb = 0; rb < NRH; ++rb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       S[wave][row][lane & 31] = acc[rb][0][r];
       S[wave][row][32 + (lane & 31)] = acc[rb][1][r];
     }
-    __syncthreads();
+    wait_lgkm0();
     if (EPI == EPI_GATE_UP) {
       // wave tile: 32 rows x 32 h-columns = 128 chunks of 8
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int c = lane + 64 * i;
         const int row = c >> 2, cc = c & 3;
-        const int tr = rb * 32 + row;
+        const int tr = (rb0 + rb) * 32 + row;
         const int64_t col = cb0 + cc * 8;
         if (tr < t.rows && col < a.n_cols) {
           const f32x4 g0 = *reinterpret_cast<const f32x4*>(&S[wave][row][cc * 8]);
@@ -391,7 +459,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
       for (int i = 0; i < 4; ++i) {
         const int c = lane + 64 * i;
         const int row = c >> 3, cc = c & 7;
-        const int tr = rb * 32 + row;
+        const int tr = (rb0 + rb) * 32 + row;
         const int64_t col = cb0 + cc * 8;
         if (tr < t.rows && col < a.n_cols) {
           const int64_t orow = t.row0 + tr;
@@ -427,16 +495,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, u
         }
       }
     }
-    __syncthreads();
+    wait_lgkm0();  // this wave's reads of its region done before the next block's writes
+  }
+  __syncthreads();  // the LDS is free for the next tile
+}
+
+template <int NR, int RB, int W, int EPI, int AMODE, bool KT>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, uint8_t* smem) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (W == 4) {
+    gemm_body<NR, NR, 4, RB, EPI, AMODE, KT>(a, t, smem, wave, 0);
+  } else {
+    if (wave < kPairs) gemm_body<NR, (NR + 1) / 2, 8, RB, EPI, AMODE, KT>(a, t, smem, wave, 0);
+    else gemm_body<NR, NR / 2, 8, RB, EPI, AMODE, KT>(a, t, smem, wave - kPairs, 1);
   }
 }
 
-// The LDS plan fills a CU, so one work-group (one wave per SIMD) runs per CU
-// and each wave may use the whole register file.
-template <int RB, int EPI, int AMODE, bool KT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+
+// The LDS plan fills a CU, so one work-group runs per CU: with 4 waves each
+// may use a SIMD's whole register file, with 8 waves half of it.
+template <int RB, int W, int EPI, int AMODE, bool KT>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4)))
 void moe_gemm_bf16(GemmArgs a, int64_t n_tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<RB>::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<RB, W>::kBytes];
   int64_t L, end, step;
   gemm::tile_range<RB * 32>(a, blockIdx.x, gridDim.x, n_tiles_n, L, end, step);
   for (; L < end; L += step) {
@@ -444,64 +525,79 @@ void moe_gemm_bf16(GemmArgs a, int64_t n_tiles_n) {
   if (!gemm::locate<RB * 32>(a, L, n_tiles_n, t)) continue;
   const int nrb = (t.rows + 31) >> 5;
   switch (nrb) {
-    case 1: gemm_tile<1, RB, EPI, AMODE, KT>(a, t, smem); break;
-    case 2: if constexpr (RB >= 2) gemm_tile<2, RB, EPI, AMODE, KT>(a, t, smem); break;
-    case 3: if constexpr (RB >= 3) gemm_tile<3, RB, EPI, AMODE, KT>(a, t, smem); break;
-    case 4: if constexpr (RB >= 4) gemm_tile<4, RB, EPI, AMODE, KT>(a, t, smem); break;
-    case 5: if constexpr (RB >= 5) gemm_tile<5, RB, EPI, AMODE, KT>(a, t, smem); break;
-    case 6: if constexpr (RB >= 6) gemm_tile<6, RB, EPI, AMODE, KT>(a, t, smem); break;
-    case 7: if constexpr (RB >= 7) gemm_tile<7, RB, EPI, AMODE, KT>(a, t, smem); break;
-    default: if constexpr (RB >= 8) gemm_tile<8, RB, EPI, AMODE, KT>(a, t, smem); break;
+    case 1: gemm_tile<1, RB, W, EPI, AMODE, KT>(a, t, smem); break;
+    case 2: if constexpr (RB >= 2) gemm_tile<2, RB, W, EPI, AMODE, KT>(a, t, smem); break;
+    case 3: if constexpr (RB >= 3) gemm_tile<3, RB, W, EPI, AMODE, KT>(a, t, smem); break;
+    case 4: if constexpr (RB >= 4) gemm_tile<4, RB, W, EPI, AMODE, KT>(a, t, smem); break;
+    case 5: if constexpr (RB >= 5) gemm_tile<5, RB, W, EPI, AMODE, KT>(a, t, smem); break;
+    case 6: if constexpr (RB >= 6) gemm_tile<6, RB, W, EPI, AMODE, KT>(a, t, smem); break;
+    case 7: if constexpr (RB >= 7) gemm_tile<7, RB, W, EPI, AMODE, KT>(a, t, smem); break;
+    default: if constexpr (RB >= 8) gemm_tile<8, RB, W, EPI, AMODE, KT>(a, t, smem); break;
   }
   }
 }
 
-template <int RB, int EPI, int AMODE, bool KT>
+template <int RB, int W, int EPI, int AMODE, bool KT>
 hipError_t launch_rb(const GemmArgs& a, int64_t mt_cap, hipStream_t s) {
   constexpr int CPW = (EPI == EPI_GATE_UP) ? 32 : 64;
-  const int64_t n_tiles_n = (a.n_cols + kWaves * CPW - 1) / (kWaves * CPW);
+  const int64_t n_tiles_n = (a.n_cols + kPairs * CPW - 1) / (kPairs * CPW);
   const int64_t mt = a.seg_off ? mt_cap
                               : (a.dense_rows + RB * 32 - 1) / (RB * 32) *
                                     (a.k_splits > 1 ? a.k_splits : 1);
   const int64_t grid = gemm::round8(mt * n_tiles_n);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  moe_gemm_bf16<RB, EPI, AMODE, KT><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a, n_tiles_n);
+  moe_gemm_bf16<RB, W, EPI, AMODE, KT><<<dim3((unsigned)grid), dim3(64 * W), 0, s>>>(a, n_tiles_n);
   return hipGetLastError();
 }
 
-// Tile heights: rb in {1, 2, 4, 6, 8} row blocks of 32.  A K that is not a
-// multiple of 64 (odd shapes only) runs the clamped variant, with rb = 1.
+// Tile heights: rb in {1, 2, 4, 6, 8} row blocks of 32; waves 8 (rb 4 and 8,
+// not the router) or 4.  A K that is not a multiple of 64 (odd shapes only)
+// runs the clamped variant, with rb = 1.
 template <int EPI, int AMODE>
-hipError_t launch_any(const GemmArgs& a, int rb, int64_t mt_cap, hipStream_t s) {
+hipError_t launch_any(const GemmArgs& a, int rb, int waves, int64_t mt_cap, hipStream_t s) {
   const bool kt = (a.K % 64) != 0 && AMODE != A_REPEAT;
   if (kt) {
     if constexpr (AMODE != A_REPEAT) {
-      if (rb == 1) return launch_rb<1, EPI, AMODE, true>(a, mt_cap, s);
+      if (rb == 1) return launch_rb<1, 4, EPI, AMODE, true>(a, mt_cap, s);
     }
     return hipErrorInvalidValue;
   }
+  const bool w8 = waves == 8 && AMODE != A_REPEAT;
   switch (rb) {
-    case 1: return launch_rb<1, EPI, AMODE, false>(a, mt_cap, s);
-    case 2: return launch_rb<2, EPI, AMODE, false>(a, mt_cap, s);
-    case 4: return launch_rb<4, EPI, AMODE, false>(a, mt_cap, s);
+    case 1: return launch_rb<1, 4, EPI, AMODE, false>(a, mt_cap, s);
+    case 2: return launch_rb<2, 4, EPI, AMODE, false>(a, mt_cap, s);
+    case 4:
+      if constexpr (AMODE != A_REPEAT) {
+        if (w8) return launch_rb<4, 8, EPI, AMODE, false>(a, mt_cap, s);
+      }
+      return launch_rb<4, 4, EPI, AMODE, false>(a, mt_cap, s);
     case 6:
-      if constexpr (AMODE != A_REPEAT) return launch_rb<6, EPI, AMODE, false>(a, mt_cap, s);
+      if constexpr (AMODE != A_REPEAT) return launch_rb<6, 4, EPI, AMODE, false>(a, mt_cap, s);
       return hipErrorInvalidValue;
-    case 8: return launch_rb<8, EPI, AMODE, false>(a, mt_cap, s);
+    case 8:
+      if constexpr (AMODE != A_REPEAT) {
+        if (w8) return launch_rb<8, 8, EPI, AMODE, false>(a, mt_cap, s);
+      }
+      return launch_rb<8, 4, EPI, AMODE, false>(a, mt_cap, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const GemmArgs& a, int epi, int amode, int rb, int64_t mt_cap,
-                            hipStream_t s) {
-  if (epi == EPI_GATE_UP && amode == A_DIRECT) return launch_any<EPI_GATE_UP, A_DIRECT>(a, rb, mt_cap, s);
-  if (epi == EPI_GATE_UP && amode == A_GATHER) return launch_any<EPI_GATE_UP, A_GATHER>(a, rb, mt_cap, s);
-  if (epi == EPI_STORE && amode == A_DIRECT) return launch_any<EPI_STORE, A_DIRECT>(a, rb, mt_cap, s);
-  if (epi == EPI_STORE_RES && amode == A_DIRECT) return launch_any<EPI_STORE_RES, A_DIRECT>(a, rb, mt_cap, s);
-  if (epi == EPI_STORE_F32 && amode == A_REPEAT) return launch_any<EPI_STORE_F32, A_REPEAT>(a, rb, mt_cap, s);
+hipError_t launch_gemm_bf16(const GemmArgs& a, int epi, int amode, int rb, int waves,
+                            int64_t mt_cap, hipStream_t s) {
+  if (epi == EPI_GATE_UP && amode == A_DIRECT)
+    return launch_any<EPI_GATE_UP, A_DIRECT>(a, rb, waves, mt_cap, s);
+  if (epi == EPI_GATE_UP && amode == A_GATHER)
+    return launch_any<EPI_GATE_UP, A_GATHER>(a, rb, waves, mt_cap, s);
+  if (epi == EPI_STORE && amode == A_DIRECT)
+    return launch_any<EPI_STORE, A_DIRECT>(a, rb, waves, mt_cap, s);
+  if (epi == EPI_STORE_RES && amode == A_DIRECT)
+    return launch_any<EPI_STORE_RES, A_DIRECT>(a, rb, waves, mt_cap, s);
+  if (epi == EPI_STORE_F32 && amode == A_REPEAT)
+    return launch_any<EPI_STORE_F32, A_REPEAT>(a, rb, waves, mt_cap, s);
   return hipErrorInvalidValue;
 }
 

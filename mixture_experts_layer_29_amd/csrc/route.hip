@@ -89,8 +89,18 @@ __global__ __launch_bounds__(kThreads) void moe_route_select(
     if (live && e < E) {
       // the router product may arrive as partial sums over K ranges: added
       // in range order, so the logit does not depend on the launch
-      float l = logits[n * E + e];
-      for (int q = 1; q < n_parts; ++q) l += logits[q * part_stride + n * E + e];
+      const float* src = logits + n * E + e;
+      float l = src[0];
+      // loads in batches of 8 (independent), then added in range order
+      for (int q0 = 1; q0 < n_parts; q0 += 8) {
+        float part[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) part[q] = q0 + q < n_parts ? src[(q0 + q) * part_stride] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (q0 + q < n_parts) l += part[q];
+        }
+      }
       s[i] = l;
       lmax = fmaxf(lmax, l);
     } else {
