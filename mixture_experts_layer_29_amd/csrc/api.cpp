@@ -124,7 +124,8 @@ struct Plan {
   size_t mt_off = 0, tile_seg = 0, perm = 0, inv_perm = 0, x_lat = 0, h = 0, out = 0;
   size_t sh_h = 0, sh_out = 0, y_lat = 0;
   int rb = 4;              // row blocks of 32 per grouped-GEMM tile (bf16)
-  int waves = 4;           // waves per grouped-GEMM work-group (bf16)
+  int waves_gate_up = 4;   // waves per grouped-GEMM work-group (bf16), gate/up
+  int waves_down = 4;      //   and down products
   int rows_per_tile = 128; // rows per grouped-GEMM m-tile
   int64_t tile_cap = 0;
   int64_t dp = 0;          // router width padded to 64
@@ -200,9 +201,12 @@ Plan make_plan(const moe_config* c, int64_t N, int call) {
   const int64_t E = c->n_experts, k = c->top_k, S = N * k;
   const size_t es = esize(c);
   p.rb = choose_rb(c, N);
-  // two waves per SIMD pay off when most tiles are full: measured on MI355X,
-  // a gain at ~170 rows per expert (K2 prefill), a small loss at ~130
-  p.waves = (p.rb == 8 && (double)N * c->top_k / (double)c->n_experts >= 160.0) ? 8 : 4;
+  // two waves per SIMD pay off when the tiles are tall: measured on MI355X,
+  // gate/up gains from ~130 rows per expert on (DeepSeek-V3 prefill), down
+  // only from ~170 (K2 prefill)
+  const double avg_rows = (double)N * c->top_k / (double)c->n_experts;
+  p.waves_gate_up = (p.rb == 8 && avg_rows >= 100.0) ? 8 : 4;
+  p.waves_down = (p.rb == 8 && avg_rows >= 160.0) ? 8 : 4;
   p.rows_per_tile = is_bf16(c) ? p.rb * 32 : moe::gemm_f32_rows_per_tile();
   p.tile_cap = S / p.rows_per_tile + (E < S ? E : S) + 1;
   p.dp = (c->d + 63) / 64 * 64;
@@ -330,7 +334,10 @@ hipError_t grouped_gemm(const moe_config* c, const Plan& p, int64_t N, const voi
   a.act = c->act;
   a.beta = c->situ_beta > 0.0f ? c->situ_beta : 1.0f;
   a.lbeta = c->situ_linear_beta;
-  if (is_bf16(c)) return moe::launch_gemm_bf16(a, epi, amode, p.rb, p.waves, p.tile_cap, s);
+  if (is_bf16(c)) {
+    const int waves = epi == moe::EPI_GATE_UP ? p.waves_gate_up : p.waves_down;
+    return moe::launch_gemm_bf16(a, epi, amode, p.rb, waves, p.tile_cap, s);
+  }
   return moe::launch_gemm_f32(a, epi, amode, p.tile_cap, s);
 }
 

@@ -264,9 +264,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
   // every few dozen cycles).
   const int rsel = lane & 31;
   const int cbase = (lane >> 5) * 4;
-  // With W = 4 the activation fragments of a K block stay in registers for its
-  // second sub-block; with W = 8 (half the registers) they are read again.
-  constexpr bool kKeepA = W == 4;
+  // The activation fragments of a K block stay in registers for its second
+  // sub-block, except with W = 8 (half the registers) beyond 3 row blocks per
+  // wave, where they are read again.
+  constexpr bool kKeepA = W == 4 || NRH <= 3;
   bf16x8 afk[kKeepA ? 4 : 2][NRA];  // activation fragments (all steps, or two)
   auto compute0 = [&](auto col_tag, const uint8_t* at, const uint8_t* bt) {
     constexpr int COL = decltype(col_tag)::value;
