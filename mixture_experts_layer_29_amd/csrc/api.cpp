@@ -202,10 +202,10 @@ Plan make_plan(const moe_config* c, int64_t N, int call) {
   const size_t es = esize(c);
   p.rb = choose_rb(c, N);
   // two waves per SIMD pay off when the tiles are tall: measured on MI355X,
-  // gate/up gains from ~130 rows per expert on (DeepSeek-V3 prefill), down
-  // only from ~170 (K2 prefill)
+  // gate/up gains with 256-row tiles (from ~130 rows per expert on), down
+  // only from ~170 rows per expert
   const double avg_rows = (double)N * c->top_k / (double)c->n_experts;
-  p.waves_gate_up = (p.rb == 8 && avg_rows >= 100.0) ? 8 : 4;
+  p.waves_gate_up = p.rb == 8 ? 8 : 4;
   p.waves_down = (p.rb == 8 && avg_rows >= 160.0) ? 8 : 4;
   p.rows_per_tile = is_bf16(c) ? p.rb * 32 : moe::gemm_f32_rows_per_tile();
   p.tile_cap = S / p.rows_per_tile + (E < S ? E : S) + 1;

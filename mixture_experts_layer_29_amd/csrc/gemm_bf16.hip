@@ -265,9 +265,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
   const int rsel = lane & 31;
   const int cbase = (lane >> 5) * 4;
   // The activation fragments of a K block stay in registers for its second
-  // sub-block, except with W = 8 (half the registers) beyond 3 row blocks per
-  // wave, where they are read again.
-  constexpr bool kKeepA = W == 4 || NRH <= 3;
+  // sub-block while they fit next to the accumulators (up to 6 row blocks
+  // with W = 4, 3 with W = 8, which has half the registers); beyond that they
+  // are read again.
+  constexpr bool kKeepA = NRH <= (W == 4 ? 6 : 3);
   bf16x8 afk[kKeepA ? 4 : 2][NRA];  // activation fragments (all steps, or two)
   auto compute0 = [&](auto col_tag, const uint8_t* at, const uint8_t* bt) {
     constexpr int COL = decltype(col_tag)::value;
@@ -577,10 +578,13 @@ hipError_t launch_any(const GemmArgs& a, int rb, int waves, int64_t mt_cap, hipS
       if constexpr (AMODE != A_REPEAT) return launch_rb<6, 4, EPI, AMODE, false>(a, mt_cap, s);
       return hipErrorInvalidValue;
     case 8:
+      // 256-row gate/up tiles always run 8 waves: with 4, their activation
+      // epilogue is too large to unroll over 8 row blocks
       if constexpr (AMODE != A_REPEAT) {
-        if (w8) return launch_rb<8, 8, EPI, AMODE, false>(a, mt_cap, s);
+        if (w8 || EPI == EPI_GATE_UP) return launch_rb<8, 8, EPI, AMODE, false>(a, mt_cap, s);
       }
-      return launch_rb<8, 4, EPI, AMODE, false>(a, mt_cap, s);
+      if constexpr (EPI != EPI_GATE_UP) return launch_rb<8, 4, EPI, AMODE, false>(a, mt_cap, s);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
