@@ -61,16 +61,18 @@ using gemm::TileLoc;
 // the instruction has no register results (nothing for the compiler to track),
 // and the compiler, seeing an LDS-DMA load in flight, would otherwise treat
 // every LDS read as unordered and wait for all of them before each MFMA.  The
-// loads are counted by the explicit vmcnt waits of the pipeline below.
+// loads are counted by the explicit vmcnt waits of the pipeline below.  An
+// LDS-DMA load must not directly follow the scalar write of m0 (one wait
+// state), hence the s_nop.
 template <bool NT>
 __device__ __forceinline__ void dma16(const void* src, const uint8_t* lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)reinterpret_cast<uintptr_t>(lds));
   if (NT) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                  :: "v"(src), "s"(m0) : "memory", "m0");
   } else {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(src), "s"(m0) : "memory", "m0");
   }
 }
@@ -89,19 +91,64 @@ constexpr int kLdsOut = 72;                         // fp32 per LDS epilogue row
 // single wave cannot feed its MFMAs from LDS (~1 KB per 34 cycles per wave on
 // gfx950).  Eight waves pay off when the tiles are mostly full.
 //
-// LDS plan of an RB-block tile: two activation stages, then as many weight
-// stages as fit (at most 9); the epilogue reuses the start of it.
+// LDS plan of a tile with NR row blocks: NA activation stages of NR x 4 KB,
+// then as many 16 KB weight stages as fit (at most 9).  Loads complete in
+// issue order, so waiting for the activations of a K block also waits for
+// every weight load issued before them: the activations are issued NA - 1
+// K blocks (2 (NA - 1) sub-iterations) ahead, far enough that the wait for
+// them does not drain the weight loads in flight.  Short tiles afford four
+// activation stages, tall ones three.
+template <int NR>
+struct Ring {
+  static constexpr int kATile = NR * 32 * kRowBytes;
+  static constexpr int kNA = NR <= 5 ? 4 : 3;
+  static constexpr int kFit = (kLdsMax - kNA * kATile) / kBStage;
+  static constexpr int kNB = kFit > 9 ? 9 : kFit;
+  static constexpr int kBytes = kNA * kATile + kNB * kBStage;
+  static_assert(kNB >= 4 && kBytes <= kLdsMax, "LDS plan");
+};
+// LDS of an RB-block kernel: the largest plan of its tiles, or the epilogue.
 template <int RB, int W = 4>
 struct Smem {
-  static constexpr int kATile = RB * 32 * kRowBytes;
-  static constexpr int kA = 2 * kATile;
-  static constexpr int kFit = (kLdsMax - kA) / kBStage;
-  static constexpr int kSB = kFit > 9 ? 9 : kFit;
-  static constexpr int kB = kSB * kBStage;
+  static constexpr int ring_max(int nr) {
+    return nr == 0 ? 0 : (ring_bytes(nr) > ring_max(nr - 1) ? ring_bytes(nr) : ring_max(nr - 1));
+  }
+  static constexpr int ring_bytes(int nr) {
+    return nr == 1 ? Ring<1>::kBytes : nr == 2 ? Ring<2>::kBytes : nr == 3 ? Ring<3>::kBytes
+         : nr == 4 ? Ring<4>::kBytes : nr == 5 ? Ring<5>::kBytes : nr == 6 ? Ring<6>::kBytes
+         : nr == 7 ? Ring<7>::kBytes : Ring<8>::kBytes;
+  }
   static constexpr int kEpi = W * 32 * kLdsOut * 4;
-  static constexpr int kBytes = (kA + kB) > kEpi ? (kA + kB) : kEpi;
+  static constexpr int kBytes = ring_max(RB) > kEpi ? ring_max(RB) : kEpi;
   static_assert(kBytes <= kLdsMax, "LDS plan exceeds one CU");
 };
+
+// vmcnt for the wait of sub-iteration u (even or odd, away from the start).
+// vmcnt counts a wave's loads in issue order, so the wait lets through the
+// loads issued after the newest one that u needs: sub-block u, issued at
+// u - (NB - 1), and for even u the activations of its K block, issued at
+// u - 2 (NA - 1).  Issue points (key 2 s + phase, in program order): with
+// W = 4, sub-iteration s issues its weights before its wait (phase 0) and,
+// for even s, its activations after its barrier (phase 1); with W = 8 both
+// come after the barrier, activations first (phase 0), and nothing of s is
+// issued before its wait.
+template <int W, int NA, int NB, int NRH, int KBL>
+constexpr int wait_count(bool even) {
+  const int u = even ? 64 : 65;
+  const int pa = W == 4 ? 1 : 0, pb = W == 4 ? 0 : 1;
+  int newest = 2 * (u - (NB - 1)) + pb;
+  if (even) {
+    const int ka = 2 * (u - 2 * (NA - 1)) + pa;
+    if (ka > newest) newest = ka;
+  }
+  const int last = W == 4 ? 2 * u + pb : 2 * u - 1;
+  int n = 0;
+  for (int key = newest + 1; key <= last; ++key) {
+    if ((key & 1) == pb) n += KBL;
+    if ((key & 1) == pa && ((key >> 1) & 1) == 0) n += NRH;
+  }
+  return n;
+}
 
 // Byte offset of 16-byte chunk `c` of row `r` in a swizzled 128-byte-row tile.
 __device__ __forceinline__ int swz(int r, int c) {
@@ -146,15 +193,15 @@ __device__ __forceinline__ void wg_barrier() {
 template <int NR, int NRH, int W, int RB, int EPI, int AMODE, bool KT>
 __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, uint8_t* smem,
                                           const int cw, const int h) {
-  constexpr int SB = Smem<RB>::kSB;
+  constexpr int SB = Ring<NR>::kNB;        // weight stages
+  constexpr int NA = Ring<NR>::kNA;        // activation stages
   constexpr int kBL = W == 8 ? 2 : 4;      // weight loads per wave per sub-block
   constexpr int NRA = NRH > 0 ? NRH : 1;   // array extents
   constexpr int C0 = W == 8 ? (NR + 1) / 2 : NR;  // row blocks of the h = 0 wave
-  static_assert(SB >= 4, "the wait counts assume weights at least three sub-blocks ahead");
   constexpr int CPW = (EPI == EPI_GATE_UP) ? 32 : 64;  // output columns per wave
-  constexpr int ATILE = Smem<RB>::kATile;
-  uint8_t* const As = smem;                            // [2][RB*32 rows][128 B]
-  uint8_t* const Bs = smem + Smem<RB>::kA;             // [SB][pair][32 rows][128 B]
+  constexpr int ATILE = Ring<NR>::kATile;
+  uint8_t* const As = smem;                            // [NA][NR*32 rows][128 B]
+  uint8_t* const Bs = smem + NA * ATILE;               // [SB][pair][32 rows][128 B]
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -222,7 +269,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
   // non-temporal, so they do not push the reused activation rows out of L2.
   const bool b_nt = a.b_stream != 0;
   auto issue_b = [&](int64_t kb, int cblk, int stage) {
-    kb = kbase + (kb >= nkb ? nkb - 1 : kb);
+    kb = kbase + (kb < 0 ? 0 : (kb >= nkb ? nkb - 1 : kb));
     uint8_t* const dst = Bs + stage * kBStage + cw * kBPair + b_base * 1024;
 #pragma unroll
     for (int i = 0; i < kBL; ++i) {
@@ -324,93 +371,74 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
     }
   };
 
-  // ---- pipeline over sub-iterations u = 2 kb + c.  Sub-iteration u first
-  // issues sub-block u + SB - 1 into stage (u - 1) % SB, then waits for its
-  // own data; for even u it then passes a work-group barrier and issues
-  // A(kb + 1) into A stage (kb+1)&1.  With W = 4 a wave alone reads its
-  // pair's slice of a weight stage, so its own program order protects the
-  // slice it refills (its reads of sub-block u - 1 are done); with W = 8 two
-  // waves share a slice and odd u has a barrier too.  The activation tile is
-  // shared, so the barrier of even u comes first (every wave's part of A(kb)
-  // has landed, and every wave has read A(kb-1), which its first sub-block
-  // keeps in registers).  The same issues happen for u = 1-SB .. -1 before the
-  // loop (the prologue; A blocks below 0 fetch A(0) again).  Per wave:
-  //  - even u needs A(kb) (issued at u-2, after that sub-iteration's weights)
-  //    and sub-block u (issued at u-SB+1 <= u-3, hence older): younger than
-  //    A(kb) are the weight loads of u-1 and u, 2 kBL (a wave without
-  //    activation loads waits a little longer than it needs);
-  //  - odd u needs sub-block u: younger are the A loads of u-SB+1 (when even),
-  //    and all loads of u-SB+2 .. u: kBL (SB-1) plus NRH at each of the
-  //    floor(SB/2) even sub-iterations among u-SB+1 .. u-1.
-  constexpr int kWaitEven = 2 * kBL;
-  constexpr int kWaitOdd = kBL * (SB - 1) + NRH * (SB / 2);
-  static_assert(kWaitOdd < 64, "vmcnt range");
-  // W = 8 keeps the order wait, barrier, issue in every sub-iteration (one
-  // barrier both publishes the sub-block and frees the stage it refills), so
-  // at a wait nothing of the current sub-iteration is issued yet:
-  //  - even u needs A(kb), the last load of u-2 (after its weights), and
-  //    sub-block u (issued at u-SB+1 <= u-3): younger are the weight loads of
-  //    u-1 only, kBL;
-  //  - odd u needs sub-block u, the first load of u-SB+1: younger are the A
-  //    loads of u-SB+1 (when even) and all loads of u-SB+2 .. u-1: kBL (SB-2)
-  //    plus NRH at each of the floor(SB/2) even sub-iterations among
-  //    u-SB+1 .. u-1.
-  constexpr int kWaitEven8 = kBL;
-  constexpr int kWaitOdd8 = kBL * (SB - 2) + NRH * (SB / 2);
+  // ---- pipeline over sub-iterations u = 2 kb + c.  Sub-iteration u reads
+  // weight stage u % SB and activation stage kb % NA; it issues sub-block
+  // u + SB - 1 into stage (u - 1) % SB and, for even u, A(kb + NA - 1) into
+  // stage (kb - 1) % NA.  The activation tile is shared by all waves, so the
+  // barrier of even u comes before its activation issue (every wave's part of
+  // A(kb) has landed, and every wave is done with A(kb - 1), whose second
+  // sub-block ended at u - 1).  With W = 4 a wave alone reads its pair's slice
+  // of a weight stage, so it issues its weights before the wait and needs no
+  // barrier at odd u (its own reads of sub-block u - 1 are done); with W = 8
+  // two waves share a slice, and every sub-iteration runs wait, barrier,
+  // issue.  The same issues happen for the sub-iterations before 0 (the
+  // prologue): blocks below 0 fetch block 0 again into stages that are
+  // refilled before anyone reads them, as blocks past the end fetch the last
+  // block into stages nobody reads.
+  constexpr int kWaitEven = wait_count<W, NA, SB, NRH, kBL>(true);
+  constexpr int kWaitOdd = wait_count<W, NA, SB, NRH, kBL>(false);
+  static_assert(kWaitEven < 64 && kWaitOdd < 64, "vmcnt range");
+  constexpr int kLead = (SB - 1) > 2 * (NA - 1) ? (SB - 1) : 2 * (NA - 1);
+  auto mod = [](int v, int m) { return ((v % m) + m) % m; };
 #pragma unroll
-  for (int q = 0; q < SB - 1; ++q) {
-    // u = q - (SB-1): sub-block u + SB - 1 = q, then for even u A(u/2 + 1),
-    // which is at most A(0): all into stage 0 (same bytes)
-    issue_b(q >> 1, q & 1, q);
-    if (((q + SB - 1) & 1) == 0) issue_a(0, 0);
+  for (int q = -kLead; q < 0; ++q) {
+    const int ub = q + SB - 1;  // sub-block issued at sub-iteration q
+    if constexpr (W == 8) {
+      if ((q & 1) == 0) issue_a(q / 2 + NA - 1, mod(q / 2 + NA - 1, NA));
+      issue_b(ub >> 1, ub & 1, mod(ub, SB));
+    } else {
+      issue_b(ub >> 1, ub & 1, mod(ub, SB));
+      if ((q & 1) == 0) issue_a(q / 2 + NA - 1, mod(q / 2 + NA - 1, NA));
+    }
   }
 
-  int sb = 0;  // stage of the sub-block being consumed
+  int sb = 0;  // weight stage of the sub-block being consumed
+  int sa = 0;  // activation stage of K block kb
   const uint8_t* const bt0 = Bs + cw * kBPair;
   for (int64_t kb = 0; kb < nkb; ++kb) {
-    const int sa = (int)(kb & 1);
+    const int sb_prev = sb == 0 ? SB - 1 : sb - 1;
+    const int sa_prev = sa == 0 ? NA - 1 : sa - 1;
     if constexpr (W == 4) {
       // c = 0
-      {
-        const int64_t ub = 2 * kb + SB - 1;
-        issue_b(ub >> 1, (SB - 1) & 1, sb == 0 ? SB - 1 : sb - 1);
-      }
+      issue_b((2 * kb + SB - 1) >> 1, (SB - 1) & 1, sb_prev);
       wait_vm<kWaitEven>();
       if (KT && AMODE != A_REPEAT && kb == nkb - 1) zero_a_tail(kb, sa);
       wg_barrier();
-      issue_a(kb + 1, sa ^ 1);
+      issue_a(kb + NA - 1, sa_prev);
       compute0(std::integral_constant<int, 0>{}, As + sa * ATILE, bt0 + sb * kBStage);
       sb = (sb + 1 == SB) ? 0 : sb + 1;
-      // c = 1: no barrier (the wave's own weight slice, A in registers)
-      {
-        const int64_t ub = 2 * kb + SB;
-        issue_b(ub >> 1, SB & 1, sb == 0 ? SB - 1 : sb - 1);
-      }
+      // c = 1: no barrier (the wave's own weight slice)
+      issue_b((2 * kb + SB) >> 1, SB & 1, sb == 0 ? SB - 1 : sb - 1);
       wait_vm<kWaitOdd>();
       compute1(As + sa * ATILE, bt0 + sb * kBStage);
       sb = (sb + 1 == SB) ? 0 : sb + 1;
     } else {
       // c = 0
-      wait_vm<kWaitEven8>();
+      wait_vm<kWaitEven>();
       if (KT && AMODE != A_REPEAT && kb == nkb - 1) zero_a_tail(kb, sa);
       wg_barrier();
-      {
-        const int64_t ub = 2 * kb + SB - 1;
-        issue_b(ub >> 1, (SB - 1) & 1, sb == 0 ? SB - 1 : sb - 1);
-      }
-      issue_a(kb + 1, sa ^ 1);
+      issue_a(kb + NA - 1, sa_prev);
+      issue_b((2 * kb + SB - 1) >> 1, (SB - 1) & 1, sb_prev);
       compute0(std::integral_constant<int, 0>{}, As + sa * ATILE, bt0 + sb * kBStage);
       sb = (sb + 1 == SB) ? 0 : sb + 1;
       // c = 1
-      wait_vm<kWaitOdd8>();
+      wait_vm<kWaitOdd>();
       wg_barrier();
-      {
-        const int64_t ub = 2 * kb + SB;
-        issue_b(ub >> 1, SB & 1, sb == 0 ? SB - 1 : sb - 1);
-      }
+      issue_b((2 * kb + SB) >> 1, SB & 1, sb == 0 ? SB - 1 : sb - 1);
       compute1(As + sa * ATILE, bt0 + sb * kBStage);
       sb = (sb + 1 == SB) ? 0 : sb + 1;
     }
+    sa = (sa + 1 == NA) ? 0 : sa + 1;
   }
   wait_vm<0>();
   __syncthreads();
