@@ -58,7 +58,7 @@ struct GemmArgs {
   const void* B0;         // weights, segment 0
   const void* B1;         // second weights (EPI_GATE_UP: up projection) or null
   int64_t b_seg_stride;   // elements between consecutive segments' weights
-  int32_t b_stream;       // 1: weights are read once (mark their loads non-temporal)
+  int32_t b_stream;       // 1: weights are read once (non-temporal loads for 32/64-row tiles)
   int64_t K;              // reduction length
   int64_t n_cols;         // output columns per segment
   const int32_t* seg_off; // [S+1] segment row offsets, or null for one dense segment

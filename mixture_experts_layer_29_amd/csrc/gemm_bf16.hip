@@ -190,7 +190,7 @@ __device__ __forceinline__ void wg_barrier() {
 // first ceil(NR/2) and the last floor(NR/2)).  It also loads NRH of the
 // tile's 4 NR activation loads (8 rows each) and 4 * 4 / (W / 4) of its
 // column pair's weight loads per sub-block.
-template <int NR, int NRH, int W, int RB, int EPI, int AMODE, bool KT>
+template <int NR, int NRH, int W, int RB, int EPI, int AMODE, bool KT, bool NT>
 __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, uint8_t* smem,
                                           const int cw, const int h) {
   constexpr int SB = Ring<NR>::kNB;        // weight stages
@@ -265,9 +265,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
       dma16<false>(ap[i] + c, dst + i * 1024);
     }
   };
-  // Weights that only this launch reads (the routed experts') are loaded
-  // non-temporal, so they do not push the reused activation rows out of L2.
-  const bool b_nt = a.b_stream != 0;
+  // NT: weights that only this launch reads (the routed experts' with short
+  // tiles) are loaded non-temporal, so they do not push the reused activation
+  // rows out of L2.
   auto issue_b = [&](int64_t kb, int cblk, int stage) {
     kb = kbase + (kb < 0 ? 0 : (kb >= nkb ? nkb - 1 : kb));
     uint8_t* const dst = Bs + stage * kBStage + cw * kBPair + b_base * 1024;
@@ -275,11 +275,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
     for (int i = 0; i < kBL; ++i) {
       int64_t off = kb * 64;
       if (KT) off = min(off, K - 8 - bchunk[i] * 8);  // A is zero there
-      if (b_nt) {
-        dma16<true>(brow[cblk][i] + off, dst + i * 1024);
-      } else {
-        dma16<false>(brow[cblk][i] + off, dst + i * 1024);
-      }
+      dma16<NT>(brow[cblk][i] + off, dst + i * 1024);
     }
   };
   // K tail: zero this lane's activation chunks of the last block that lie past K
@@ -530,21 +526,21 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
   __syncthreads();  // the LDS is free for the next tile
 }
 
-template <int NR, int RB, int W, int EPI, int AMODE, bool KT>
+template <int NR, int RB, int W, int EPI, int AMODE, bool KT, bool NT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, uint8_t* smem) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (W == 4) {
-    gemm_body<NR, NR, 4, RB, EPI, AMODE, KT>(a, t, smem, wave, 0);
+    gemm_body<NR, NR, 4, RB, EPI, AMODE, KT, NT>(a, t, smem, wave, 0);
   } else {
-    if (wave < kPairs) gemm_body<NR, (NR + 1) / 2, 8, RB, EPI, AMODE, KT>(a, t, smem, wave, 0);
-    else gemm_body<NR, NR / 2, 8, RB, EPI, AMODE, KT>(a, t, smem, wave - kPairs, 1);
+    if (wave < kPairs) gemm_body<NR, (NR + 1) / 2, 8, RB, EPI, AMODE, KT, NT>(a, t, smem, wave, 0);
+    else gemm_body<NR, NR / 2, 8, RB, EPI, AMODE, KT, NT>(a, t, smem, wave - kPairs, 1);
   }
 }
 
 
 // The LDS plan fills a CU, so one work-group runs per CU: with 4 waves each
 // may use a SIMD's whole register file, with 8 waves half of it.
-template <int RB, int W, int EPI, int AMODE, bool KT>
+template <int RB, int W, int EPI, int AMODE, bool KT, bool NT>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4)))
 void moe_gemm_bf16(GemmArgs a, int64_t n_tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<RB, W>::kBytes];
@@ -555,19 +551,19 @@ void moe_gemm_bf16(GemmArgs a, int64_t n_tiles_n) {
   if (!gemm::locate<RB * 32>(a, L, n_tiles_n, t)) continue;
   const int nrb = (t.rows + 31) >> 5;
   switch (nrb) {
-    case 1: gemm_tile<1, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    case 2: if constexpr (RB >= 2) gemm_tile<2, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    case 3: if constexpr (RB >= 3) gemm_tile<3, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    case 4: if constexpr (RB >= 4) gemm_tile<4, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    case 5: if constexpr (RB >= 5) gemm_tile<5, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    case 6: if constexpr (RB >= 6) gemm_tile<6, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    case 7: if constexpr (RB >= 7) gemm_tile<7, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    default: if constexpr (RB >= 8) gemm_tile<8, RB, W, EPI, AMODE, KT>(a, t, smem); break;
+    case 1: gemm_tile<1, RB, W, EPI, AMODE, KT, NT>(a, t, smem); break;
+    case 2: if constexpr (RB >= 2) gemm_tile<2, RB, W, EPI, AMODE, KT, NT>(a, t, smem); break;
+    case 3: if constexpr (RB >= 3) gemm_tile<3, RB, W, EPI, AMODE, KT, NT>(a, t, smem); break;
+    case 4: if constexpr (RB >= 4) gemm_tile<4, RB, W, EPI, AMODE, KT, NT>(a, t, smem); break;
+    case 5: if constexpr (RB >= 5) gemm_tile<5, RB, W, EPI, AMODE, KT, NT>(a, t, smem); break;
+    case 6: if constexpr (RB >= 6) gemm_tile<6, RB, W, EPI, AMODE, KT, NT>(a, t, smem); break;
+    case 7: if constexpr (RB >= 7) gemm_tile<7, RB, W, EPI, AMODE, KT, NT>(a, t, smem); break;
+    default: if constexpr (RB >= 8) gemm_tile<8, RB, W, EPI, AMODE, KT, NT>(a, t, smem); break;
   }
   }
 }
 
-template <int RB, int W, int EPI, int AMODE, bool KT>
+template <int RB, int W, int EPI, int AMODE, bool KT, bool NT = false>
 hipError_t launch_rb(const GemmArgs& a, int64_t mt_cap, hipStream_t s) {
   constexpr int CPW = (EPI == EPI_GATE_UP) ? 32 : 64;
   const int64_t n_tiles_n = (a.n_cols + kPairs * CPW - 1) / (kPairs * CPW);
@@ -577,7 +573,7 @@ hipError_t launch_rb(const GemmArgs& a, int64_t mt_cap, hipStream_t s) {
   const int64_t grid = gemm::round8(mt * n_tiles_n);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  moe_gemm_bf16<RB, W, EPI, AMODE, KT><<<dim3((unsigned)grid), dim3(64 * W), 0, s>>>(a, n_tiles_n);
+  moe_gemm_bf16<RB, W, EPI, AMODE, KT, NT><<<dim3((unsigned)grid), dim3(64 * W), 0, s>>>(a, n_tiles_n);
   return hipGetLastError();
 }
 
@@ -595,8 +591,12 @@ hipError_t launch_any(const GemmArgs& a, int rb, int waves, int64_t mt_cap, hipS
   }
   const bool w8 = waves == 8 && AMODE != A_REPEAT;
   switch (rb) {
-    case 1: return launch_rb<1, 4, EPI, AMODE, false>(a, mt_cap, s);
-    case 2: return launch_rb<2, 4, EPI, AMODE, false>(a, mt_cap, s);
+    case 1:
+      if (a.b_stream) return launch_rb<1, 4, EPI, AMODE, false, true>(a, mt_cap, s);
+      return launch_rb<1, 4, EPI, AMODE, false>(a, mt_cap, s);
+    case 2:
+      if (a.b_stream) return launch_rb<2, 4, EPI, AMODE, false, true>(a, mt_cap, s);
+      return launch_rb<2, 4, EPI, AMODE, false>(a, mt_cap, s);
     case 4:
       if constexpr (AMODE != A_REPEAT) {
         if (w8) return launch_rb<4, 8, EPI, AMODE, false>(a, mt_cap, s);
