@@ -10,25 +10,27 @@
 // time, and each weight byte feeds only the T_e rows routed to its expert, so
 // the kernel is built to stream every expert's weights once at close to full
 // HBM bandwidth with the MFMAs for its rows running underneath:
-//  - a work-group (4 waves) owns one (segment, n-tile, m-tile); tiles are up to
-//    RB x 32 rows high so that a whole expert segment usually fits one tile
-//    (every extra m-tile of an expert would stream its weights again);
-//  - each wave owns two 32-column blocks of the output (the gate and the up
-//    block of the same columns for the gate/up product);
+//  - a work-group owns one (segment, n-tile, m-tile); tiles are up to RB x 32
+//    rows high so that a whole expert segment usually fits one tile (every
+//    extra m-tile of an expert would stream its weights again);
+//  - four column pairs per tile, each of two 32-column blocks of the output
+//    (the gate and the up block of the same columns for the gate/up product);
+//    with 4 waves a wave owns a pair, with 8 (two per SIMD) the two waves of a
+//    pair split its row blocks;
 //  - both operands are copied from HBM straight into LDS by the load units
 //    (global_load_lds_dwordx4: 16 bytes per lane, 8 lanes per 128-byte piece
 //    of a row, no registers held while in flight).  The weights stream as
-//    sub-blocks of one 32-column block x 64 k per wave (16 KB per work-group),
+//    sub-blocks of one 32-column block x 64 k per pair (16 KB per work-group),
 //    SB-1 sub-blocks ahead in an SB-stage ring; the activations of a 64-k block
-//    serve its two column sub-blocks and are loaded one block ahead.  Under
-//    full load HBM latency is several microseconds, so the bytes in flight per
-//    CU ((SB-1) x 16 KB, 80-128 KB) set the achievable bandwidth, and each
-//    visit of a weight row reads a whole 128-byte piece (shorter pieces cost
-//    DRAM efficiency);
+//    serve its two column sub-blocks and are loaded NA-1 blocks ahead in NA
+//    stages (the ring plan depends on the tile's row blocks).  Each visit of a
+//    weight row reads a whole 128-byte piece (shorter pieces cost DRAM
+//    efficiency);
 //  - waits are explicit vmcnt counts followed by a plain work-group barrier, so
 //    loads for later sub-blocks stay in flight.  Every sub-iteration issues the
-//    same loads (past either end of K the last block is fetched again into the
-//    stage that is free), so the counts are compile-time constants;
+//    same loads (past either end of K the last block is fetched again into a
+//    stage nobody reads), so the counts are compile-time constants, derived
+//    from the issue order;
 //  - LDS tiles are unpadded 128-byte rows whose 16-byte chunks are
 //    XOR-swizzled by bits 1..3 of the row (each lane fetches the chunk that
 //    belongs at its fixed LDS slot): the MFMA-layout reads touch all 64 banks
@@ -39,8 +41,9 @@
 //    tile with few rows issues only the MFMAs (and activation loads) it needs;
 //  - in gather mode activation rows are read through the dispatch
 //    permutation, so no expert-sorted copy of the input is ever written;
-//  - tiles are numbered segment-major, then n-tile, then m-tile, and mapped to
-//    work-group ids so that consecutive tiles land on the same XCD;
+//  - tiles are numbered segment-major, then n-tile, then m-tile; the experts
+//    are split into 8 runs of about equal cost, one per XCD, so the n-tiles
+//    of an expert share its activation rows in one L2;
 //  - the epilogue stages the fp32 accumulators through LDS, applies
 //    SiLU/SiTU-and-mul or the residual add in fp32, rounds once and writes
 //    16-byte row-contiguous chunks.
