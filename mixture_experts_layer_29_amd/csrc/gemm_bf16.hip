@@ -53,6 +53,7 @@
 #include <type_traits>
 
 #include "gemm_common.h"
+#include "gemm_plan.h"
 
 namespace moe {
 namespace {
@@ -80,12 +81,7 @@ __device__ __forceinline__ void dma16(const void* src, const uint8_t* lds) {
   }
 }
 
-constexpr int kPairs = 4;                           // column pairs (32+32 columns) per tile
-constexpr int kRowBytes = 128;                      // one 64-element K block of a bf16 row
-constexpr int kBRows = 32;                          // weight rows of a column pair per sub-block
-constexpr int kBPair = kBRows * kRowBytes;          // 4 KB
-constexpr int kBStage = kPairs * kBPair;            // 16 KB
-constexpr int kLdsMax = 160 * 1024;                 // LDS of one CU
+using namespace plan;
 constexpr int kLdsOut = 72;                         // fp32 per LDS epilogue row: 64 + 8 pad
 
 // Waves per work-group, W: 4 (one per column pair and SIMD), or, for tiles of
@@ -94,22 +90,6 @@ constexpr int kLdsOut = 72;                         // fp32 per LDS epilogue row
 // single wave cannot feed its MFMAs from LDS (~1 KB per 34 cycles per wave on
 // gfx950).  Eight waves pay off when the tiles are mostly full.
 //
-// LDS plan of a tile with NR row blocks: NA activation stages of NR x 4 KB,
-// then as many 16 KB weight stages as fit (at most 9).  Loads complete in
-// issue order, so waiting for the activations of a K block also waits for
-// every weight load issued before them: the activations are issued NA - 1
-// K blocks (2 (NA - 1) sub-iterations) ahead, far enough that the wait for
-// them does not drain the weight loads in flight.  Short tiles afford four
-// activation stages, tall ones three.
-template <int NR>
-struct Ring {
-  static constexpr int kATile = NR * 32 * kRowBytes;
-  static constexpr int kNA = NR <= 5 ? 4 : 3;
-  static constexpr int kFit = (kLdsMax - kNA * kATile) / kBStage;
-  static constexpr int kNB = kFit > 9 ? 9 : kFit;
-  static constexpr int kBytes = kNA * kATile + kNB * kBStage;
-  static_assert(kNB >= 4 && kBytes <= kLdsMax, "LDS plan");
-};
 // LDS of an RB-block kernel: the largest plan of its tiles, or the epilogue.
 template <int RB, int W = 4>
 struct Smem {
@@ -125,33 +105,6 @@ struct Smem {
   static constexpr int kBytes = ring_max(RB) > kEpi ? ring_max(RB) : kEpi;
   static_assert(kBytes <= kLdsMax, "LDS plan exceeds one CU");
 };
-
-// vmcnt for the wait of sub-iteration u (even or odd, away from the start).
-// vmcnt counts a wave's loads in issue order, so the wait lets through the
-// loads issued after the newest one that u needs: sub-block u, issued at
-// u - (NB - 1), and for even u the activations of its K block, issued at
-// u - 2 (NA - 1).  Issue points (key 2 s + phase, in program order): with
-// W = 4, sub-iteration s issues its weights before its wait (phase 0) and,
-// for even s, its activations after its barrier (phase 1); with W = 8 both
-// come after the barrier, activations first (phase 0), and nothing of s is
-// issued before its wait.
-template <int W, int NA, int NB, int NRH, int KBL>
-constexpr int wait_count(bool even) {
-  const int u = even ? 64 : 65;
-  const int pa = W == 4 ? 1 : 0, pb = W == 4 ? 0 : 1;
-  int newest = 2 * (u - (NB - 1)) + pb;
-  if (even) {
-    const int ka = 2 * (u - 2 * (NA - 1)) + pa;
-    if (ka > newest) newest = ka;
-  }
-  const int last = W == 4 ? 2 * u + pb : 2 * u - 1;
-  int n = 0;
-  for (int key = newest + 1; key <= last; ++key) {
-    if ((key & 1) == pb) n += KBL;
-    if ((key & 1) == pa && ((key >> 1) & 1) == 0) n += NRH;
-  }
-  return n;
-}
 
 // Byte offset of 16-byte chunk `c` of row `r` in a swizzled 128-byte-row tile.
 __device__ __forceinline__ int swz(int r, int c) {
