@@ -128,8 +128,8 @@ def cpu_baseline(w, seconds):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the expert-parallel design is described, not built)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(expert parallelism is a design, not an implementation)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

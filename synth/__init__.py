@@ -7,7 +7,7 @@ or device memory (``libsynth_dev.so``) with the counter-based generator defined 
 ``synth_core.h``.  Both fillers produce the same bits for the same element, so the
 oracle can regenerate on the host exactly the inputs the GPU was given.
 
-Distributions (variances read as stated in the design doc): hidden ~ N(0,1); router
+Distributions (variances, the plainest reading of the pages' init): hidden ~ N(0,1); router
 weight ~ N(0, 1/d); correction bias ~ N(0, 0.01^2), or for the skewed latent
 workload a Zipf rank profile 0.25 * r^-1.1 over a seeded permutation of the
 experts; gate/up weights ~ N(0, 1/d_in); down weights ~ N(0, 1/d_ff); shared and
