@@ -184,6 +184,22 @@ moe_status moe_expert_gate_up(const moe_config* cfg, int64_t N, const void* x_so
                               void* stream);
 
 /*
+ * moe_expert_gate_up_gather - moe_expert_gate_up with the row gather of
+ * moe_permute folded into its activation loads ([K3-ADD] moe_infer gathers
+ * x[argsort // k] before the expert loop): row p of expert e is
+ * x_in[perm[p] / k], so no sorted copy of the input is written.  This is the
+ * form moe_block_forward runs.
+ * x_in [N, d_in] dtype; perm [N*k] int32 as moe_permute writes it (every value
+ * in [0, N*k); other values are clamped to a valid row); expert_offsets, w1,
+ * w3 and the output h_sorted [N*k, d_ff] as for moe_expert_gate_up.  Needs the
+ * workspace of MOE_CALL_GATE_UP.
+ */
+moe_status moe_expert_gate_up_gather(const moe_config* cfg, int64_t N, const void* x_in,
+                                     const int32_t* perm, const int32_t* expert_offsets,
+                                     const void* w1, const void* w3, void* h_sorted,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_expert_down - second half of every routed expert ([K3-GATE] expert:
  * w2 applied to the activation).  out_sorted[p] = w2[e] . h_sorted[p] for the
  * rows p of expert e, fp32 accumulation, rounded once to dtype.
@@ -215,9 +231,13 @@ moe_status moe_combine(const moe_config* cfg, int64_t N, const void* out_sorted,
  * (x_in = hidden . w_down^T, rounded to dtype), else x_in = hidden; permute,
  * gate/up, down and combine as above; with d_latent > 0 RMS-normalise each
  * combined row in fp32 (y / sqrt(mean(y^2) + norm_eps) * gamma, when
- * latent_norm) and project it up with w_up; with d_ff_shared > 0 add the
- * shared expert (the same gated MLP and activation, on the full-width hidden)
- * before the single final rounding.
+ * latent_norm), round it to dtype (the up projection's operand) and project
+ * it up with w_up; with d_ff_shared > 0 add the shared expert (the same gated
+ * MLP and activation, on the full-width hidden; its output is kept in fp32)
+ * to the combined or up-projected sum in fp32, before the single final
+ * rounding of y.  Intermediate roundings to dtype: the latent input x_in, each
+ * expert's h and output rows, the shared expert's h, and the normalised
+ * latent row.
  * hidden [N, d] dtype.  Out: y [N, d] dtype.  Optional outputs (NULL skips):
  * topk_idx_out [N, k] int32, topk_weight_out [N, k] fp32,
  * tokens_per_expert_out [E] int32.

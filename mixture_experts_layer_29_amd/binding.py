@@ -96,11 +96,13 @@ def lib():
         L.moe_route.argtypes = [C, i64, P, P, P, P, P, P, sz, P]
         L.moe_permute.argtypes = [C, i64, P, P, P, P, P, P, P, P, sz, P]
         L.moe_expert_gate_up.argtypes = [C, i64, P, P, P, P, P, P, sz, P]
+        L.moe_expert_gate_up_gather.argtypes = [C, i64, P, P, P, P, P, P, P, sz, P]
         L.moe_expert_down.argtypes = [C, i64, P, P, P, P, P, sz, P]
         L.moe_combine.argtypes = [C, i64, P, P, P, P, P, P]
         L.moe_block_forward.argtypes = [C, i64, ctypes.POINTER(moe_weights), P, P, P, P, P, P, sz, P]
         for f in ("moe_validate_config", "moe_workspace_size", "moe_route", "moe_permute",
-                  "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_block_forward"):
+                  "moe_expert_gate_up", "moe_expert_gate_up_gather", "moe_expert_down",
+                  "moe_combine", "moe_block_forward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -177,6 +179,13 @@ def moe_permute(cfg, N, topk_idx, x_in, tokens_per_expert, expert_offsets, perm,
 def moe_expert_gate_up(cfg, N, x_sorted, expert_offsets, w1, w3, h_sorted, ws, stream=None):
     _check(lib().moe_expert_gate_up(ctypes.byref(cfg), N, _p(x_sorted), _p(expert_offsets), _p(w1),
                                     _p(w3), _p(h_sorted), _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_expert_gate_up_gather(cfg, N, x_in, perm, expert_offsets, w1, w3, h_sorted, ws,
+                              stream=None):
+    _check(lib().moe_expert_gate_up_gather(ctypes.byref(cfg), N, _p(x_in), _p(perm),
+                                           _p(expert_offsets), _p(w1), _p(w3), _p(h_sorted),
+                                           _p(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_expert_down(cfg, N, h_sorted, expert_offsets, w2, out_sorted, ws, stream=None):

@@ -242,7 +242,7 @@ Plan make_plan(const moe_config* c, int64_t N, int call) {
     }
     if (c->d_ff_shared > 0) {
       p.sh_h = cv.take((size_t)N * c->d_ff_shared * es);
-      p.sh_out = cv.take((size_t)N * c->d * es);
+      p.sh_out = cv.take((size_t)N * c->d * 4);  // fp32: added before the final rounding
     }
   }
   p.bytes = cv.off;
@@ -467,14 +467,15 @@ moe_status moe_permute(const moe_config* cfg, int64_t N, const int32_t* topk_idx
 }
 
 static moe_status expert_call(const moe_config* cfg, int64_t N, const void* A,
-                              const int32_t* expert_offsets, const void* B0, const void* B1,
-                              void* C, void* workspace, size_t workspace_bytes, void* stream,
-                              bool gate_up, const char* fn) {
+                              const int32_t* perm, const int32_t* expert_offsets, const void* B0,
+                              const void* B1, void* C, void* workspace, size_t workspace_bytes,
+                              void* stream, bool gate_up, const char* fn) {
   moe_status st = validate(cfg, fn);
   if (st != MOE_OK) return st;
   if ((st = validate_n(cfg, N, fn)) != MOE_OK) return st;
   if (N == 0) return ok();
   REQUIRE_PTR(A);
+  if (perm) REQUIRE_PTR(perm);
   REQUIRE_PTR(expert_offsets);
   REQUIRE_PTR(B0);
   if (gate_up) REQUIRE_PTR(B1);
@@ -486,7 +487,10 @@ static moe_status expert_call(const moe_config* cfg, int64_t N, const void* A,
                                            at<int32_t>(workspace, p.mt_off),
                                            at<int32_t>(workspace, p.tile_seg), p.tile_cap, s));
   const int64_t d_in = d_in_of(cfg);
-  if (gate_up) {
+  if (gate_up && perm) {
+    CHECK_HIP(grouped_gemm(cfg, p, N, A, moe::A_GATHER, perm, N, d_in, expert_offsets, B0, B1,
+                           cfg->d_ff, C, moe::EPI_GATE_UP, workspace, s));
+  } else if (gate_up) {
     CHECK_HIP(grouped_gemm(cfg, p, N, A, moe::A_DIRECT, nullptr, N * cfg->top_k, d_in,
                            expert_offsets, B0, B1, cfg->d_ff, C, moe::EPI_GATE_UP, workspace, s));
   } else {
@@ -500,15 +504,25 @@ moe_status moe_expert_gate_up(const moe_config* cfg, int64_t N, const void* x_so
                               const int32_t* expert_offsets, const void* w1, const void* w3,
                               void* h_sorted, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  return expert_call(cfg, N, x_sorted, expert_offsets, w1, w3, h_sorted, workspace,
+  return expert_call(cfg, N, x_sorted, nullptr, expert_offsets, w1, w3, h_sorted, workspace,
                      workspace_bytes, stream, true, "moe_expert_gate_up");
+}
+
+moe_status moe_expert_gate_up_gather(const moe_config* cfg, int64_t N, const void* x_in,
+                                     const int32_t* perm, const int32_t* expert_offsets,
+                                     const void* w1, const void* w3, void* h_sorted,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_expert_gate_up_gather";
+  if (N > 0 && !perm) return fail(MOE_ERR_INVALID_ARG, "%s: perm is NULL", fn);
+  return expert_call(cfg, N, x_in, perm, expert_offsets, w1, w3, h_sorted, workspace,
+                     workspace_bytes, stream, true, fn);
 }
 
 moe_status moe_expert_down(const moe_config* cfg, int64_t N, const void* h_sorted,
                            const int32_t* expert_offsets, const void* w2, void* out_sorted,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  return expert_call(cfg, N, h_sorted, expert_offsets, w2, nullptr, out_sorted, workspace,
-                     workspace_bytes, stream, false, "moe_expert_down");
+  return expert_call(cfg, N, h_sorted, nullptr, expert_offsets, w2, nullptr, out_sorted,
+                     workspace, workspace_bytes, stream, false, "moe_expert_down");
 }
 
 moe_status moe_combine(const moe_config* cfg, int64_t N, const void* out_sorted,
@@ -525,7 +539,8 @@ moe_status moe_combine(const moe_config* cfg, int64_t N, const void* out_sorted,
   REQUIRE_PTR(y);
   if (residual && !aligned16(residual))
     return fail(MOE_ERR_INVALID_ARG, "%s: residual is not 16-byte aligned", fn);
-  CHECK_HIP(moe::launch_combine(out_sorted, inv_perm, topk_weight, residual, y, N, cfg->top_k,
+  CHECK_HIP(moe::launch_combine(out_sorted, inv_perm, topk_weight, residual,
+                                is_bf16(cfg) ? 0 : 1, y, N, cfg->top_k,
                                 d_in_of(cfg), N * cfg->top_k, is_bf16(cfg) ? 1 : 0,
                                 static_cast<hipStream_t>(stream)));
   return ok();
@@ -610,8 +625,9 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
     sh_out = at<void>(ws, p.sh_out);
     CHECK_HIP(dense_gemm(cfg, hidden, N, d, w->sh_w1, w->sh_w3, cfg->d_ff_shared, sh_h,
                          moe::EPI_GATE_UP, nullptr, s));
+    // the shared output stays in fp32 until the single final rounding
     CHECK_HIP(dense_gemm(cfg, sh_h, N, cfg->d_ff_shared, w->sh_w2, nullptr, d, sh_out,
-                         moe::EPI_STORE, nullptr, s));
+                         is_bf16(cfg) ? moe::EPI_STORE_F32 : moe::EPI_STORE, nullptr, s));
   }
 
   CHECK_HIP(mark(MOE_STAGE_SHARED, s));
@@ -634,7 +650,8 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
     CHECK_HIP(dense_gemm(cfg, y_lat, N, L, w->w_up, nullptr, d, y,
                          sh_out ? moe::EPI_STORE_RES : moe::EPI_STORE, sh_out, s));
   } else {
-    CHECK_HIP(moe::launch_combine(out, inv, wts, sh_out, y, N, (int)k, d, S, is_bf16(cfg) ? 1 : 0, s));
+    CHECK_HIP(moe::launch_combine(out, inv, wts, sh_out, 1, y, N, (int)k, d, S,
+                                  is_bf16(cfg) ? 1 : 0, s));
   }
   CHECK_HIP(mark(MOE_STAGE_END, s));
   return ok();

@@ -6,10 +6,10 @@
 // One work-group per token row.  The k expert rows are read through inv_perm,
 // multiplied by their weights and summed in fp32 in slot order j = 0..k-1 (a
 // fixed order: results do not depend on scheduling), a residual row (the
-// shared expert's output) is added, and the sum is rounded once.  The latent
-// variant keeps the fp32 row in registers, forms its mean square with a
-// fixed-shape tree, and applies y / sqrt(mean(y^2) + eps) * gamma before the
-// single rounding.
+// shared expert's output, kept in fp32 by the block) is added, and the sum is
+// rounded once.  The latent variant keeps the fp32 row in registers, forms its
+// mean square with a fixed-shape tree, and applies y / sqrt(mean(y^2) + eps) *
+// gamma before the single rounding.
 #include "common.h"
 
 namespace moe {
@@ -72,7 +72,7 @@ __device__ __forceinline__ void weighted_sum(const void* out_sorted, const int32
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool RES_F32>
 __global__ __launch_bounds__(kThreads) void moe_combine(const void* __restrict__ out_sorted,
                                                         const int32_t* __restrict__ inv_perm,
                                                         const float* __restrict__ wts,
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void moe_combine(const void* __restrict__
     weighted_sum<BF16>(out_sorted, pos, w, k, width, c, acc);
     if (residual) {
       float r[kVec];
-      load8<BF16>(residual, n * width + c, r);
+      load8<BF16 && !RES_F32>(residual, n * width + c, r);
 #pragma unroll
       for (int i = 0; i < kVec; ++i) acc[i] += r[i];
     }
@@ -155,15 +155,18 @@ __global__ __launch_bounds__(kThreads) void moe_combine_rmsnorm(
 }  // namespace
 
 hipError_t launch_combine(const void* out_sorted, const int32_t* inv_perm, const float* w,
-                          const void* residual, void* y, int64_t N, int k, int64_t width,
-                          int64_t rows, int bf16, hipStream_t s) {
+                          const void* residual, int res_f32, void* y, int64_t N, int k,
+                          int64_t width, int64_t rows, int bf16, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  if (bf16) {
-    moe_combine<true><<<dim3((unsigned)N), dim3(kThreads), 0, s>>>(out_sorted, inv_perm, w, residual,
-                                                                   y, N, k, width, rows);
+  const dim3 g((unsigned)N), b(kThreads);
+  if (bf16 && res_f32) {
+    moe_combine<true, true><<<g, b, 0, s>>>(out_sorted, inv_perm, w, residual, y, N, k, width, rows);
+  } else if (bf16) {
+    moe_combine<true, false><<<g, b, 0, s>>>(out_sorted, inv_perm, w, residual, y, N, k, width,
+                                             rows);
   } else {
-    moe_combine<false><<<dim3((unsigned)N), dim3(kThreads), 0, s>>>(out_sorted, inv_perm, w,
-                                                                    residual, y, N, k, width, rows);
+    moe_combine<false, true><<<g, b, 0, s>>>(out_sorted, inv_perm, w, residual, y, N, k, width,
+                                             rows);
   }
   return hipGetLastError();
 }

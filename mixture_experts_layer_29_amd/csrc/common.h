@@ -38,7 +38,7 @@ enum Epi : int {
   EPI_STORE = 0,       // C = acc (rounded to the output type)
   EPI_STORE_F32 = 1,   // C = acc as fp32 (router logits)
   EPI_GATE_UP = 2,     // C = act(acc_gate, acc_up), B0 = gate, B1 = up
-  EPI_STORE_RES = 3,   // C = acc + residual (one rounding)
+  EPI_STORE_RES = 3,   // C = acc + residual (fp32 residual, one rounding)
 };
 
 enum AMode : int {
@@ -74,7 +74,7 @@ struct GemmArgs {
   void* C;                // output
   int64_t ldc;
   int64_t c_rows;         // rows of C: tile rows at or past it are never touched
-  const void* residual;   // EPI_STORE_RES
+  const void* residual;   // EPI_STORE_RES: fp32 [rows, ld_res]
   int64_t ld_res;
   int32_t act;            // EPI_GATE_UP activation
   float beta;             // SiTU beta
@@ -122,9 +122,10 @@ hipError_t launch_tiles_from_offsets(const int32_t* offsets, int64_t E, int rows
 
 // ---------------------------------------------------------------------------
 // Combine.
+// residual: [N, width] of the output type, or fp32 when res_f32 (or NULL)
 hipError_t launch_combine(const void* out_sorted, const int32_t* inv_perm, const float* w,
-                          const void* residual, void* y, int64_t N, int k, int64_t width,
-                          int64_t rows, int bf16, hipStream_t s);
+                          const void* residual, int res_f32, void* y, int64_t N, int k,
+                          int64_t width, int64_t rows, int bf16, hipStream_t s);
 hipError_t launch_combine_rmsnorm(const void* out_sorted, const int32_t* inv_perm, const float* w,
                                   const float* gamma, float eps, int norm, void* y, int64_t N,
                                   int k, int64_t width, int64_t rows, int bf16, hipStream_t s);

@@ -159,7 +159,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
   uint8_t* const As = smem;                            // [NA][NR*32 rows][128 B]
   uint8_t* const Bs = smem + NA * ATILE;               // [SB][pair][32 rows][128 B]
 
-  const int tid = threadIdx.x;
+  // The thread id passes through an opaque move at the start of every tile, so
+  // the per-lane row and chunk indices below are recomputed per tile (a few ALU
+  // ops) rather than hoisted out of the tile loop for every tile height of the
+  // switch and held in registers across it (which made the 8-wave forms spill).
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int rb0 = h ? C0 : 0;                          // first row block of this wave
   const int a_base = h ? kPairs * C0 + cw * NRH : cw * NRH;  // first activation load
@@ -448,24 +453,24 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
           f32x4 v0 = *reinterpret_cast<const f32x4*>(&S[wave][row][cc * 8]);
           f32x4 v1 = *reinterpret_cast<const f32x4*>(&S[wave][row][cc * 8 + 4]);
           if (EPI == EPI_STORE_F32) {
-            // router logits: any expert count, so scalar stores up to n_cols;
-            // a split-K range writes its own partial product
+            // fp32 output (router logits, the shared expert's output); a
+            // split-K range writes its own partial product.  Any column count
+            // (the router's is the expert count): scalar stores at a ragged end.
             float* dst = static_cast<float*>(a.C) + t.split * a.c_split_stride + orow * a.ldc + col;
+            if (col + 8 <= a.n_cols && ((a.ldc | col) & 3) == 0) {
+              *reinterpret_cast<f32x4*>(dst) = v0;
+              *reinterpret_cast<f32x4*>(dst + 4) = v1;
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              if (col + e < a.n_cols) dst[e] = e < 4 ? v0[e] : v1[e - 4];
+              for (int e = 0; e < 8; ++e) {
+                if (col + e < a.n_cols) dst[e] = e < 4 ? v0[e] : v1[e - 4];
+              }
             }
           } else {
             if (EPI == EPI_STORE_RES) {
-              const u32x4 rq = *reinterpret_cast<const u32x4*>(
-                  static_cast<const bf16_t*>(a.residual) + orow * a.ld_res + col);
-#pragma unroll
-              for (int e = 0; e < 2; ++e) {
-                v0[2 * e] += __uint_as_float(rq[e] << 16);
-                v0[2 * e + 1] += __uint_as_float(rq[e] & 0xFFFF0000u);
-                v1[2 * e] += __uint_as_float(rq[2 + e] << 16);
-                v1[2 * e + 1] += __uint_as_float(rq[2 + e] & 0xFFFF0000u);
-              }
+              const float* rp = static_cast<const float*>(a.residual) + orow * a.ld_res + col;
+              v0 += *reinterpret_cast<const f32x4*>(rp);
+              v1 += *reinterpret_cast<const f32x4*>(rp + 4);
             }
             u32x4 o;
             o[0] = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
@@ -585,6 +590,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int epi, int amode, int rb, int w
     return launch_any<EPI_STORE, A_DIRECT>(a, rb, waves, mt_cap, s);
   if (epi == EPI_STORE_RES && amode == A_DIRECT)
     return launch_any<EPI_STORE_RES, A_DIRECT>(a, rb, waves, mt_cap, s);
+  if (epi == EPI_STORE_F32 && amode == A_DIRECT)
+    return launch_any<EPI_STORE_F32, A_DIRECT>(a, rb, waves, mt_cap, s);
   if (epi == EPI_STORE_F32 && amode == A_REPEAT)
     return launch_any<EPI_STORE_F32, A_REPEAT>(a, rb, waves, mt_cap, s);
   return hipErrorInvalidValue;

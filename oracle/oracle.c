@@ -71,9 +71,6 @@ static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
 
 /* ------------------------------------------------------------------ router */
 
-/* [K2-AFF] / [V32-AFF]: logits = linear(x.float(), weight.float()) with no
- * bias term; scores = logits.sigmoid(); the choice scores add the per-expert
- * correction bias. */
 /* [K2-AFF] / [V32-AFF] gate forward: logits = x . W_r^T in fp32 (the fp64 sum
  * rounded once to fp32); score = sigmoid(logit), or ([V32-AFF]) the softmax of
  * the token's logits over all experts; choice = score + bias when the router

@@ -134,6 +134,22 @@ def test_block_argument_errors():
     assert st == binding.MOE_ERR_INVALID_ARG
 
 
+def test_gathered_gate_up_argument_errors():
+    lib = binding.lib()
+    c = good(dtype=m.DTYPE_BF16)
+    st = lib.moe_expert_gate_up_gather(ctypes.byref(c), 8, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, 1 << 30, None)
+    assert st == binding.MOE_ERR_INVALID_ARG and "perm" in binding.last_error()
+    st = lib.moe_expert_gate_up_gather(ctypes.byref(c), 8, FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, 1 << 30, None)
+    assert st == binding.MOE_ERR_INVALID_ARG and "perm" in binding.last_error()
+    st = lib.moe_expert_gate_up_gather(ctypes.byref(c), 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, 16, None)
+    assert st == binding.MOE_ERR_WORKSPACE
+    assert lib.moe_expert_gate_up_gather(ctypes.byref(c), 0, None, None, None, None, None, None,
+                                         None, 0, None) == binding.MOE_OK
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     c = good()
