@@ -121,7 +121,11 @@ def test_expert_rows_full_size(name):
         xr = x_in[perm[r0:r1] // w.k]
         h_ref = oracle.gate_up_rows(ocfg, {e: synth.host_tensor(w, "w1", expert=e)},
                                     {e: synth.host_tensor(w, "w3", expert=e)}, xr, erow)
-        r_h, m_h = assert_close_bf16(as_f64(to_host(h[r0:r1])), h_ref, f"{name} gate/up e={e}")
+        # h is stored in bf16: an element beyond 12.8 rms moves by more than 5e-2 rms
+        # from that rounding alone (h's tail reaches ~15 rms here), so each element
+        # is allowed half a bf16 ulp of its own magnitude on top of the bar
+        r_h, m_h = assert_close_bf16(as_f64(to_host(h[r0:r1])), h_ref, f"{name} gate/up e={e}",
+                                     output_rounding_slack=True)
         hr = host_rows(w.d_ff, r0, r1, H_SEED, H_TID, H_STD)
         o_ref = oracle.down_rows(ocfg, {e: synth.host_tensor(w, "w2", expert=e)}, hr, erow)
         r_o, m_o = assert_close_bf16(as_f64(to_host(out[r0:r1])), o_ref, f"{name} down e={e}")
