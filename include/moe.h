@@ -167,6 +167,24 @@ moe_status moe_permute(const moe_config* cfg, int64_t N, const int32_t* topk_idx
                        size_t workspace_bytes, void* stream);
 
 /*
+ * moe_permute_static - moe_permute for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments and results without a workspace.  Its
+ * scratch (the dispatch masks and per-chunk bases, ceil(N/64) * E * 12 bytes
+ * plus alignment) lives in a static device array of MOE_STATIC_SCRATCH_BYTES
+ * that each GPU the library runs on holds until the process ends.  Larger
+ * problems return MOE_ERR_UNSUPPORTED before anything is enqueued.  The call
+ * allocates nothing.  Every call on one GPU shares that GPU's array: calls that
+ * may overlap on one GPU (different streams, no ordering between them) race
+ * and give unspecified results; calls ordered on one stream are safe.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (8u << 20)
+moe_status moe_permute_static(const moe_config* cfg, int64_t N, const int32_t* topk_idx,
+                              const void* x_in, int32_t* tokens_per_expert,
+                              int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm,
+                              void* x_sorted, void* stream);
+
+/*
  * moe_expert_gate_up - first half of every routed expert ([K3-GATE] expert
  * and situ excerpts), on the expert-sorted rows.  For each expert e and row p
  * in [expert_offsets[e], expert_offsets[e+1]):

@@ -6,5 +6,5 @@ from .binding import (  # noqa: F401
     ACT_SILU, ACT_SITU, CALL_BLOCK, CALL_COMBINE, CALL_DOWN, CALL_GATE_UP, CALL_PERMUTE,
     CALL_ROUTE, DTYPE_BF16, DTYPE_F32, MoeError, Weights, make_config, moe_block_forward,
     moe_combine, moe_expert_down, moe_expert_gate_up, moe_expert_gate_up_gather, moe_permute,
-    moe_route,
-    moe_validate_config, moe_workspace_size, status_str, workspace)
+    moe_permute_static, moe_route, moe_validate_config, moe_workspace_size, status_str,
+    workspace)

@@ -95,12 +95,14 @@ def lib():
         L.moe_workspace_size.argtypes = [C, i64, i32, ctypes.POINTER(sz)]
         L.moe_route.argtypes = [C, i64, P, P, P, P, P, P, sz, P]
         L.moe_permute.argtypes = [C, i64, P, P, P, P, P, P, P, P, sz, P]
+        L.moe_permute_static.argtypes = [C, i64, P, P, P, P, P, P, P, P]
         L.moe_expert_gate_up.argtypes = [C, i64, P, P, P, P, P, P, sz, P]
         L.moe_expert_gate_up_gather.argtypes = [C, i64, P, P, P, P, P, P, P, sz, P]
         L.moe_expert_down.argtypes = [C, i64, P, P, P, P, P, sz, P]
         L.moe_combine.argtypes = [C, i64, P, P, P, P, P, P]
         L.moe_block_forward.argtypes = [C, i64, ctypes.POINTER(moe_weights), P, P, P, P, P, P, sz, P]
         for f in ("moe_validate_config", "moe_workspace_size", "moe_route", "moe_permute",
+                  "moe_permute_static",
                   "moe_expert_gate_up", "moe_expert_gate_up_gather", "moe_expert_down",
                   "moe_combine", "moe_block_forward"):
             getattr(L, f).restype = ctypes.c_int
@@ -174,6 +176,14 @@ def moe_permute(cfg, N, topk_idx, x_in, tokens_per_expert, expert_offsets, perm,
     _check(lib().moe_permute(ctypes.byref(cfg), N, _p(topk_idx), _p(x_in), _p(tokens_per_expert),
                              _p(expert_offsets), _p(perm), _p(inv_perm), _p(x_sorted), _p(ws),
                              _nbytes(ws), _stream(stream)))
+
+
+def moe_permute_static(cfg, N, topk_idx, x_in, tokens_per_expert, expert_offsets, perm,
+                       inv_perm, x_sorted, stream=None):
+    """moe_permute with its scratch in the library's static device array (no workspace)."""
+    _check(lib().moe_permute_static(ctypes.byref(cfg), N, _p(topk_idx), _p(x_in),
+                                    _p(tokens_per_expert), _p(expert_offsets), _p(perm),
+                                    _p(inv_perm), _p(x_sorted), _stream(stream)))
 
 
 def moe_expert_gate_up(cfg, N, x_sorted, expert_offsets, w1, w3, h_sorted, ws, stream=None):

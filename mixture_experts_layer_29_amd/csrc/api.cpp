@@ -10,10 +10,18 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
 #include "common.h"
+
+// Scratch of moe_permute_static: one array per GPU, alive until the process
+// ends.  Host code never uses the array's name as an address (on the host it
+// is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current and
+// kept per device (static_scratch below).
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -377,6 +385,27 @@ moe_status run_route(const moe_config* c, int64_t N, const void* hidden, const f
   return MOE_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status static_scratch(void** out, const char* fn) {
+  int dev = -1;
+  CHECK_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d is beyond the %d supported", fn, dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    CHECK_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return fail(MOE_ERR_HIP, "%s: no device address for the static scratch", fn);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -430,11 +459,10 @@ moe_status moe_route(const moe_config* cfg, int64_t N, const void* hidden, const
   return st == MOE_OK ? ok() : st;
 }
 
-moe_status moe_permute(const moe_config* cfg, int64_t N, const int32_t* topk_idx, const void* x_in,
-                       int32_t* tokens_per_expert, int32_t* expert_offsets, int32_t* perm,
-                       int32_t* inv_perm, void* x_sorted, void* workspace, size_t workspace_bytes,
-                       void* stream) {
-  const char* fn = "moe_permute";
+static moe_status permute_args(const moe_config* cfg, int64_t N, const int32_t* topk_idx,
+                               const void* x_in, const int32_t* tokens_per_expert,
+                               const int32_t* expert_offsets, const int32_t* perm,
+                               const int32_t* inv_perm, const void* x_sorted, const char* fn) {
   moe_status st = validate(cfg, fn);
   if (st != MOE_OK) return st;
   if ((st = validate_n(cfg, N, fn)) != MOE_OK) return st;
@@ -449,13 +477,21 @@ moe_status moe_permute(const moe_config* cfg, int64_t N, const int32_t* topk_idx
       REQUIRE_PTR(x_sorted);
     }
   }
-  const Plan p = make_plan(cfg, N, MOE_CALL_PERMUTE);
-  if ((st = check_ws(p, workspace, workspace_bytes, fn)) != MOE_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return MOE_OK;
+}
+
+// Dispatch launches with the masks and chunk bases at `scratch` (laid out by
+// the plan of MOE_CALL_PERMUTE).  Every entry of both is written before it is
+// read, so the scratch needs no clearing.
+static moe_status run_permute(const moe_config* cfg, int64_t N, const int32_t* topk_idx,
+                              const void* x_in, int32_t* tokens_per_expert,
+                              int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm,
+                              void* x_sorted, void* scratch, const Plan& p, hipStream_t s,
+                              const char* fn) {
   const int64_t E = cfg->n_experts;
   const int k = cfg->top_k;
-  uint64_t* bits = at<uint64_t>(workspace, p.bits);
-  int32_t* base = at<int32_t>(workspace, p.base);
+  uint64_t* bits = at<uint64_t>(scratch, p.bits);
+  int32_t* base = at<int32_t>(scratch, p.base);
   CHECK_HIP(moe::launch_dispatch_mask(topk_idx, N, k, E, bits, s));
   CHECK_HIP(moe::launch_dispatch_scan(bits, p.n_chunks, E, tokens_per_expert, expert_offsets, base,
                                       0, nullptr, nullptr, 0, s));
@@ -464,6 +500,40 @@ moe_status moe_permute(const moe_config* cfg, int64_t N, const int32_t* topk_idx
     CHECK_HIP(moe::launch_gather_rows(x_in, N, d_in_of(cfg), (int)esize(cfg), perm, k, N * k,
                                       x_sorted, s));
   return ok();
+}
+
+moe_status moe_permute(const moe_config* cfg, int64_t N, const int32_t* topk_idx, const void* x_in,
+                       int32_t* tokens_per_expert, int32_t* expert_offsets, int32_t* perm,
+                       int32_t* inv_perm, void* x_sorted, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  const char* fn = "moe_permute";
+  moe_status st = permute_args(cfg, N, topk_idx, x_in, tokens_per_expert, expert_offsets, perm,
+                               inv_perm, x_sorted, fn);
+  if (st != MOE_OK) return st;
+  const Plan p = make_plan(cfg, N, MOE_CALL_PERMUTE);
+  if ((st = check_ws(p, workspace, workspace_bytes, fn)) != MOE_OK) return st;
+  return run_permute(cfg, N, topk_idx, x_in, tokens_per_expert, expert_offsets, perm, inv_perm,
+                     x_sorted, workspace, p, static_cast<hipStream_t>(stream), fn);
+}
+
+moe_status moe_permute_static(const moe_config* cfg, int64_t N, const int32_t* topk_idx,
+                              const void* x_in, int32_t* tokens_per_expert,
+                              int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm,
+                              void* x_sorted, void* stream) {
+  const char* fn = "moe_permute_static";
+  moe_status st = permute_args(cfg, N, topk_idx, x_in, tokens_per_expert, expert_offsets, perm,
+                               inv_perm, x_sorted, fn);
+  if (st != MOE_OK) return st;
+  const Plan p = make_plan(cfg, N, MOE_CALL_PERMUTE);
+  if (p.bytes > MOE_STATIC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: N=%lld tokens over E=%lld experts need %zu bytes of dispatch scratch; the "
+                "static scratch holds %zu (ceil(N/64) * E * 12 bytes must fit)", fn, (long long)N,
+                (long long)cfg->n_experts, p.bytes, (size_t)MOE_STATIC_SCRATCH_BYTES);
+  void* ptr = nullptr;  // this device's copy of the static scratch
+  if ((st = static_scratch(&ptr, fn)) != MOE_OK) return st;
+  return run_permute(cfg, N, topk_idx, x_in, tokens_per_expert, expert_offsets, perm, inv_perm,
+                     x_sorted, ptr, p, static_cast<hipStream_t>(stream), fn);
 }
 
 static moe_status expert_call(const moe_config* cfg, int64_t N, const void* A,
