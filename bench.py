@@ -45,7 +45,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 STAGES = ["route", "latent_down", "dispatch", "shared", "gate_up", "down", "combine"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the sources whose code the routed grouped-GEMM launches run
-GEMM_SOURCES = ["common.h", "gemm_common.h", "gemm_plan.h", "gemm_bf16.hip"]
+GEMM_SOURCES = ["common.h", "gemm_common.h", "gemm_plan.h", "gemm_lds.h", "gemm_bf16.hip"]
 
 
 def gemm_source_digest() -> str:

@@ -324,11 +324,10 @@ hipError_t grouped_gemm(const moe_config* c, const Plan& p, int64_t N, const voi
   a.B0 = B0;
   a.B1 = B1;
   a.b_seg_stride = n_cols * K;
-  // every expert's weights are read once per launch: with short tiles
-  // (decode-like loads) non-temporal weight loads keep the activations in L2
-  // and raise the weight stream to ~6.7 TB/s on MI355X; with tall tiles the
-  // gain in gate/up was cancelled by a slower down product, so they stay off.
-  a.b_stream = p.rb <= 2 ? 1 : 0;
+  // an expert's weights are read by its own tiles only: non-temporal loads
+  // for experts whose rows fit one m-tile (cached for the others, whose
+  // m-tiles share them in L2)
+  a.b_stream = 2;
   a.K = K;
   a.n_cols = n_cols;
   a.seg_off = seg_off;

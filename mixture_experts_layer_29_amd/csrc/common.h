@@ -58,7 +58,8 @@ struct GemmArgs {
   const void* B0;         // weights, segment 0
   const void* B1;         // second weights (EPI_GATE_UP: up projection) or null
   int64_t b_seg_stride;   // elements between consecutive segments' weights
-  int32_t b_stream;       // 1: weights are read once (non-temporal loads for 32/64-row tiles)
+  int32_t b_stream;       // weight loads: 0 cached; 1 non-temporal; 2 non-temporal for a
+                          // segment of one m-tile (its weights are read by no other tile)
   int64_t K;              // reduction length
   int64_t n_cols;         // output columns per segment
   const int32_t* seg_off; // [S+1] segment row offsets, or null for one dense segment

@@ -47,6 +47,7 @@ __device__ __forceinline__ float act_pair(int act, float g, float u, float beta,
 
 struct TileLoc {
   int64_t seg;
+  int64_t mt;     // m-tiles of the segment (grouped), 0 for a dense product
   int64_t row0;   // first row of the tile in the concatenated row space
   int rows;       // rows of the tile that exist (1 .. BM)
   int64_t j;      // n-tile
@@ -75,6 +76,7 @@ __device__ __forceinline__ bool locate(const GemmArgs& a, int64_t L, int64_t n_t
     const int64_t s0 = a.seg_off[seg];
     const int64_t s1 = min((int64_t)a.seg_off[seg + 1], a.c_rows);
     t.seg = seg;
+    t.mt = mt;
     t.row0 = s0 + i * BM;
     t.rows = (int)min((int64_t)BM, s1 - t.row0);
     t.j = j;
@@ -92,6 +94,7 @@ __device__ __forceinline__ bool locate(const GemmArgs& a, int64_t L, int64_t n_t
   const int64_t j = L / mt, i = L - j * mt;
   const int64_t nkb = (a.K + 63) >> 6;
   t.seg = 0;
+  t.mt = 0;
   t.row0 = i * BM;
   t.rows = (int)min((int64_t)BM, a.dense_rows - t.row0);
   t.j = j;
