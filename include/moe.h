@@ -73,7 +73,9 @@ typedef enum {
   MOE_CALL_GATE_UP = 2,
   MOE_CALL_DOWN = 3,
   MOE_CALL_COMBINE = 4,
-  MOE_CALL_BLOCK = 5
+  MOE_CALL_BLOCK = 5,
+  MOE_CALL_SHARED = 6,
+  MOE_CALL_LATENT = 7
 } moe_call;
 
 /* Block configuration; field names follow the pages' config fields. */
@@ -229,19 +231,62 @@ moe_status moe_expert_down(const moe_config* cfg, int64_t N, const void* h_sorte
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_expert_down_scatter - moe_expert_down with the un-permute of [K3-ADD]
+ * moe_infer (the outputs put back at their tokens' places before the weighted
+ * sum) folded into its stores: the output row of sorted row p goes to slot
+ * perm[p] = n*k + j, so out_slots holds each token's k expert rows
+ * contiguously, in slot order.  The form moe_block_forward runs.
+ * h_sorted, expert_offsets, w2 as for moe_expert_down; perm [N*k] int32 as
+ * moe_permute writes it (a permutation of 0 .. N*k - 1: every slot is written
+ * once).  Out: out_slots [N*k, d_in] dtype.  Workspace of MOE_CALL_DOWN.
+ */
+moe_status moe_expert_down_scatter(const moe_config* cfg, int64_t N, const void* h_sorted,
+                                   const int32_t* expert_offsets, const int32_t* perm,
+                                   const void* w2, void* out_slots, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * moe_combine - back to token order and weighted sum ([K3-ADD] moe_infer: the
  * un-permute, the product with the routing weights in their fp32 precision,
  * the sum over the k slots, the cast back).
- *   y[n] = residual[n] + sum_{j = 0..k-1} topk_weight[n][j] *
- *          out_sorted[inv_perm[n*k + j]],
- *   accumulated in fp32 in that fixed j order, rounded once to dtype.
- * out_sorted [N*k, d_in] dtype; inv_perm [N*k] int32; topk_weight [N, k] fp32;
- * residual [N, d_in] dtype or NULL (zero).  Out: y [N, d_in] dtype.
- * Needs no workspace.
+ *   y[n] = residual[n] + sum_{j = 0..k-1} topk_weight[n][j] * row(n, j),
+ *   row(n, j) = out_sorted[inv_perm[n*k + j]], or, with inv_perm NULL (rows
+ *   already in slot order, as moe_expert_down_scatter writes them),
+ *   out_sorted[n*k + j]; accumulated in fp32 in that fixed j order, rounded
+ *   once to dtype.
+ * out_sorted [N*k, d_in] dtype; inv_perm [N*k] int32 or NULL; topk_weight
+ * [N, k] fp32; residual [N, d_in] dtype or NULL (zero).  Out: y [N, d_in]
+ * dtype.  Needs no workspace.
  */
 moe_status moe_combine(const moe_config* cfg, int64_t N, const void* out_sorted,
                        const int32_t* inv_perm, const float* topk_weight, const void* residual,
                        void* y, void* stream);
+
+/*
+ * moe_shared_expert - the shared expert ([K3-ADD] forward: the shared experts
+ * run on the block's full-width input and their output is added to the routed
+ * sum): out = sh_w2 . act(sh_w1 . hidden, sh_w3 . hidden), the same gated MLP
+ * and activation as the routed experts (fp32 accumulation, activation in
+ * fp32, its result rounded once to dtype), the output kept in fp32 (as
+ * moe_block_forward adds it before its final rounding).
+ * Needs cfg->d_ff_shared > 0.  hidden [N, d] dtype; sh_w1, sh_w3
+ * [d_ff_shared, d] dtype; sh_w2 [d, d_ff_shared] dtype.  Out: out [N, d] fp32.
+ * Workspace: moe_workspace_size(MOE_CALL_SHARED).
+ */
+moe_status moe_shared_expert(const moe_config* cfg, int64_t N, const void* hidden,
+                             const void* sh_w1, const void* sh_w3, const void* sh_w2, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_latent_project - a latent projection of the K3 latent block ([K3-ADD]
+ * forward): up = 0, the down projection x_lat = hidden . w_down^T (x [N, d],
+ * w [d_latent, d], out [N, d_latent]); up = 1, the up projection
+ * y = y_lat . w_up^T (+ residual) (x [N, d_latent], w [d, d_latent],
+ * out [N, d]).  fp32 accumulation; residual [N, n_out] fp32 or NULL, added in
+ * fp32; the sum rounded once to dtype.  Needs cfg->d_latent > 0.  No workspace.
+ */
+moe_status moe_latent_project(const moe_config* cfg, int64_t N, int32_t up, const void* x,
+                              const void* w, const float* residual, void* out, void* stream);
 
 /*
  * moe_block_forward - the whole block ([K3-ADD] forward): route on the

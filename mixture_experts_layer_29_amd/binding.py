@@ -19,7 +19,8 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 ACT_SILU, ACT_SITU = 0, 1
 SCORE_SIGMOID, SCORE_SOFTMAX = 0, 1
 TOPK_NOAUX_TC = 0
-CALL_ROUTE, CALL_PERMUTE, CALL_GATE_UP, CALL_DOWN, CALL_COMBINE, CALL_BLOCK = range(6)
+CALL_ROUTE, CALL_PERMUTE, CALL_GATE_UP, CALL_DOWN, CALL_COMBINE, CALL_BLOCK, CALL_SHARED, \
+    CALL_LATENT = range(8)
 
 
 class MoeError(RuntimeError):
@@ -99,12 +100,15 @@ def lib():
         L.moe_expert_gate_up.argtypes = [C, i64, P, P, P, P, P, P, sz, P]
         L.moe_expert_gate_up_gather.argtypes = [C, i64, P, P, P, P, P, P, P, sz, P]
         L.moe_expert_down.argtypes = [C, i64, P, P, P, P, P, sz, P]
+        L.moe_expert_down_scatter.argtypes = [C, i64, P, P, P, P, P, P, sz, P]
         L.moe_combine.argtypes = [C, i64, P, P, P, P, P, P]
         L.moe_block_forward.argtypes = [C, i64, ctypes.POINTER(moe_weights), P, P, P, P, P, P, sz, P]
+        L.moe_shared_expert.argtypes = [C, i64, P, P, P, P, P, P, sz, P]
+        L.moe_latent_project.argtypes = [C, i64, i32, P, P, P, P, P]
         for f in ("moe_validate_config", "moe_workspace_size", "moe_route", "moe_permute",
                   "moe_permute_static",
                   "moe_expert_gate_up", "moe_expert_gate_up_gather", "moe_expert_down",
-                  "moe_combine", "moe_block_forward"):
+                  "moe_expert_down_scatter", "moe_combine", "moe_block_forward", "moe_shared_expert", "moe_latent_project"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -203,7 +207,28 @@ def moe_expert_down(cfg, N, h_sorted, expert_offsets, w2, out_sorted, ws, stream
                                  _p(out_sorted), _p(ws), _nbytes(ws), _stream(stream)))
 
 
+def moe_expert_down_scatter(cfg, N, h_sorted, expert_offsets, perm, w2, out_slots, ws,
+                            stream=None):
+    """moe_expert_down writing row p to slot perm[p] (token order, k rows per token)."""
+    _check(lib().moe_expert_down_scatter(ctypes.byref(cfg), N, _p(h_sorted), _p(expert_offsets),
+                                         _p(perm), _p(w2), _p(out_slots), _p(ws), _nbytes(ws),
+                                         _stream(stream)))
+
+
+def moe_shared_expert(cfg, N, hidden, sh_w1, sh_w3, sh_w2, out, ws, stream=None):
+    """out [N, d] fp32 = the shared expert's MLP on hidden."""
+    _check(lib().moe_shared_expert(ctypes.byref(cfg), N, _p(hidden), _p(sh_w1), _p(sh_w3),
+                                   _p(sh_w2), _p(out), _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_latent_project(cfg, N, up, x, w, residual, out, stream=None):
+    """The latent down (up=0) or up (up=1) projection, with an optional fp32 residual."""
+    _check(lib().moe_latent_project(ctypes.byref(cfg), N, int(up), _p(x), _p(w), _p(residual),
+                                    _p(out), _stream(stream)))
+
+
 def moe_combine(cfg, N, out_sorted, inv_perm, topk_weight, residual, y, stream=None):
+    """inv_perm None: out_sorted holds the rows in slot order (moe_expert_down_scatter)."""
     _check(lib().moe_combine(ctypes.byref(cfg), N, _p(out_sorted), _p(inv_perm), _p(topk_weight),
                              _p(residual), _p(y), _stream(stream)))
 

@@ -169,6 +169,8 @@ int choose_rb(const moe_config* c, int64_t N) {
   return 1;
 }
 
+constexpr int64_t kDenseMinRows = 512;
+
 // Dense products (shared expert, latent projections) reuse every weight tile
 // across all m-tiles, so they are bound by the operand traffic into each CU
 // rather than by HBM: the tallest tile that still gives every CU a tile has
@@ -234,6 +236,7 @@ Plan make_plan(const moe_config* c, int64_t N, int call) {
     p.mt_off = cv.take((size_t)(E + 1 + 9) * 4);  // m-tile prefix, then the XCD split
     p.tile_seg = cv.take((size_t)p.tile_cap * 4);
   }
+  if (call == MOE_CALL_SHARED) p.sh_h = cv.take((size_t)N * c->d_ff_shared * es);
   if (block) {
     const int64_t d_in = d_in_of(c);
     p.idx = cv.take((size_t)S * 4);
@@ -304,7 +307,11 @@ hipError_t dense_gemm(const moe_config* c, const void* A, int64_t rows, int64_t 
   a.beta = c->situ_beta > 0.0f ? c->situ_beta : 1.0f;
   a.lbeta = c->situ_linear_beta;
   if (is_bf16(c)) {
-    // dense tiles are full: two waves per SIMD from 4 row blocks up
+    // from 512 rows on, the MFMA-bound tile kernel; short products (decode)
+    // are bound by their weights and stream them with the grouped kernel's
+    // tiles, the tallest that still give every CU a tile
+    if (rows >= kDenseMinRows && moe::gemm_dense_supported(a, epi))
+      return moe::launch_gemm_dense(a, epi, s);
     const int rb = dense_rb(rows, K, n_cols, epi);
     return moe::launch_gemm_bf16(a, epi, moe::A_DIRECT, rb, rb >= 4 ? 8 : 4, 0, s);
   }
@@ -314,7 +321,7 @@ hipError_t dense_gemm(const moe_config* c, const void* A, int64_t rows, int64_t 
 hipError_t grouped_gemm(const moe_config* c, const Plan& p, int64_t N, const void* A, int amode,
                         const int32_t* a_map, int64_t a_rows, int64_t K, const int32_t* seg_off,
                         const void* B0, const void* B1, int64_t n_cols, void* C, int epi,
-                        void* ws, hipStream_t s) {
+                        void* ws, hipStream_t s, const int32_t* c_map = nullptr) {
   moe::GemmArgs a = gemm_args();
   a.A = A;
   a.lda = K;
@@ -336,6 +343,7 @@ hipError_t grouped_gemm(const moe_config* c, const Plan& p, int64_t N, const voi
   a.tile_seg = at<int32_t>(ws, p.tile_seg);
   a.tile_cap = p.tile_cap;
   a.C = C;
+  a.c_map = c_map;
   a.ldc = n_cols;
   a.c_rows = N * c->top_k;
   a.act = c->act;
@@ -346,6 +354,16 @@ hipError_t grouped_gemm(const moe_config* c, const Plan& p, int64_t N, const voi
     return moe::launch_gemm_bf16(a, epi, amode, p.rb, waves, p.tile_cap, s);
   }
   return moe::launch_gemm_f32(a, epi, amode, p.tile_cap, s);
+}
+
+// Shared expert: h = act(x . sh_w1^T, x . sh_w3^T) rounded to the block dtype,
+// then out = h . sh_w2^T kept in fp32.
+hipError_t shared_expert(const moe_config* c, int64_t N, const void* x, const void* w1,
+                         const void* w3, const void* w2, void* h, float* out, hipStream_t s) {
+  hipError_t e = dense_gemm(c, x, N, c->d, w1, w3, c->d_ff_shared, h, moe::EPI_GATE_UP, nullptr, s);
+  if (e != hipSuccess) return e;
+  return dense_gemm(c, h, N, c->d_ff_shared, w2, nullptr, c->d, out,
+                    is_bf16(c) ? moe::EPI_STORE_F32 : moe::EPI_STORE, nullptr, s);
 }
 
 moe_status run_route(const moe_config* c, int64_t N, const void* hidden, const float* w_router,
@@ -405,6 +423,40 @@ moe_status static_scratch(void** out, const char* fn) {
   return MOE_OK;
 }
 
+// The block runs its shared expert on a side stream of the device, beside
+// the routed path: the shared expert's products are bound by the matrix
+// cores, the routed expert GEMMs by HBM, so the two share the GPU better than
+// they run one after the other.  One side stream (default priority) and a
+// fork/join event pair per device, created on first use and kept until the
+// process ends.  A block call holds g_side_mutex from its fork to its join,
+// so concurrent calls do not interleave their records of the two events.
+constexpr bool kSharedOnSide = true;
+struct Side {
+  hipStream_t stream;
+  hipEvent_t fork, join;
+};
+std::mutex g_side_mutex;
+Side g_side[kMaxDevices] = {};
+
+// The current device's side stream; the caller holds g_side_mutex.
+moe_status side_stream(Side* out, const char* fn) {
+  int dev = -1;
+  CHECK_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d is beyond the %d supported", fn, dev,
+                kMaxDevices);
+  Side& sd = g_side[dev];
+  if (!sd.stream) {
+    Side n{};
+    CHECK_HIP(hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking));
+    CHECK_HIP(hipEventCreateWithFlags(&n.fork, hipEventDisableTiming));
+    CHECK_HIP(hipEventCreateWithFlags(&n.join, hipEventDisableTiming));
+    sd = n;
+  }
+  *out = sd;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -433,7 +485,9 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t N, int32_t call, si
   if (st != MOE_OK) return st;
   if ((st = validate_n(cfg, N, fn)) != MOE_OK) return st;
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
-  if (call < MOE_CALL_ROUTE || call > MOE_CALL_BLOCK) return fail(MOE_ERR_INVALID_ARG, "%s: unknown call %d", fn, call);
+  if (call < MOE_CALL_ROUTE || call > MOE_CALL_LATENT) return fail(MOE_ERR_INVALID_ARG, "%s: unknown call %d", fn, call);
+  if (call == MOE_CALL_SHARED && cfg->d_ff_shared <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: the config has no shared expert", fn);
   *bytes = make_plan(cfg, N, call).bytes;
   return ok();
 }
@@ -563,8 +617,10 @@ static moe_status expert_call(const moe_config* cfg, int64_t N, const void* A,
     CHECK_HIP(grouped_gemm(cfg, p, N, A, moe::A_DIRECT, nullptr, N * cfg->top_k, d_in,
                            expert_offsets, B0, B1, cfg->d_ff, C, moe::EPI_GATE_UP, workspace, s));
   } else {
+    // down: with perm, row p is written to its slot perm[p]
     CHECK_HIP(grouped_gemm(cfg, p, N, A, moe::A_DIRECT, nullptr, N * cfg->top_k, cfg->d_ff,
-                           expert_offsets, B0, nullptr, d_in, C, moe::EPI_STORE, workspace, s));
+                           expert_offsets, B0, nullptr, d_in, C, moe::EPI_STORE, workspace, s,
+                           perm));
   }
   return ok();
 }
@@ -594,6 +650,16 @@ moe_status moe_expert_down(const moe_config* cfg, int64_t N, const void* h_sorte
                      workspace, workspace_bytes, stream, false, "moe_expert_down");
 }
 
+moe_status moe_expert_down_scatter(const moe_config* cfg, int64_t N, const void* h_sorted,
+                                   const int32_t* expert_offsets, const int32_t* perm,
+                                   const void* w2, void* out_slots, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_expert_down_scatter";
+  if (N > 0 && !perm) return fail(MOE_ERR_INVALID_ARG, "%s: perm is NULL", fn);
+  return expert_call(cfg, N, h_sorted, perm, expert_offsets, w2, nullptr, out_slots, workspace,
+                     workspace_bytes, stream, false, fn);
+}
+
 moe_status moe_combine(const moe_config* cfg, int64_t N, const void* out_sorted,
                        const int32_t* inv_perm, const float* topk_weight, const void* residual,
                        void* y, void* stream) {
@@ -603,7 +669,6 @@ moe_status moe_combine(const moe_config* cfg, int64_t N, const void* out_sorted,
   if ((st = validate_n(cfg, N, fn)) != MOE_OK) return st;
   if (N == 0) return ok();
   REQUIRE_PTR(out_sorted);
-  REQUIRE_PTR(inv_perm);
   REQUIRE_PTR(topk_weight);
   REQUIRE_PTR(y);
   if (residual && !aligned16(residual))
@@ -612,6 +677,47 @@ moe_status moe_combine(const moe_config* cfg, int64_t N, const void* out_sorted,
                                 is_bf16(cfg) ? 0 : 1, y, N, cfg->top_k,
                                 d_in_of(cfg), N * cfg->top_k, is_bf16(cfg) ? 1 : 0,
                                 static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+moe_status moe_shared_expert(const moe_config* cfg, int64_t N, const void* hidden,
+                             const void* sh_w1, const void* sh_w3, const void* sh_w2, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_shared_expert";
+  moe_status st = validate(cfg, fn);
+  if (st != MOE_OK) return st;
+  if ((st = validate_n(cfg, N, fn)) != MOE_OK) return st;
+  if (cfg->d_ff_shared <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: the config has no shared expert", fn);
+  if (N == 0) return ok();
+  REQUIRE_PTR(hidden);
+  REQUIRE_PTR(sh_w1);
+  REQUIRE_PTR(sh_w3);
+  REQUIRE_PTR(sh_w2);
+  REQUIRE_PTR(out);
+  const Plan p = make_plan(cfg, N, MOE_CALL_SHARED);
+  if ((st = check_ws(p, workspace, workspace_bytes, fn)) != MOE_OK) return st;
+  CHECK_HIP(shared_expert(cfg, N, hidden, sh_w1, sh_w3, sh_w2, at<void>(workspace, p.sh_h), out,
+                          static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+moe_status moe_latent_project(const moe_config* cfg, int64_t N, int32_t up, const void* x,
+                              const void* w, const float* residual, void* out, void* stream) {
+  const char* fn = "moe_latent_project";
+  moe_status st = validate(cfg, fn);
+  if (st != MOE_OK) return st;
+  if ((st = validate_n(cfg, N, fn)) != MOE_OK) return st;
+  if (cfg->d_latent <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: the config has no latent width", fn);
+  if (up != 0 && up != 1) return fail(MOE_ERR_INVALID_ARG, "%s: up=%d must be 0 or 1", fn, up);
+  if (N == 0) return ok();
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(out);
+  OPTIONAL_PTR(residual);
+  const int64_t K = up ? cfg->d_latent : cfg->d, n_out = up ? cfg->d : cfg->d_latent;
+  const int epi = residual ? moe::EPI_STORE_RES : moe::EPI_STORE;
+  CHECK_HIP(dense_gemm(cfg, x, N, K, w, nullptr, n_out, out, epi, residual,
+                       static_cast<hipStream_t>(stream)));
   return ok();
 }
 
@@ -662,8 +768,25 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
   int32_t* perm = at<int32_t>(ws, p.perm);
   int32_t* inv = at<int32_t>(ws, p.inv_perm);
 
-  // router on the full-width input
+  // shared expert on the full-width input, forked to the side stream (or run
+  // in line below); joined before the output that adds it
   CHECK_HIP(mark(MOE_STAGE_BEGIN, s));
+  void* sh_out = nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  Side side{};
+  const bool on_side = kSharedOnSide && cfg->d_ff_shared > 0;
+  if (cfg->d_ff_shared > 0) sh_out = at<void>(ws, p.sh_out);
+  if (on_side) {
+    side_lock = std::unique_lock<std::mutex>(g_side_mutex);
+    if ((st = side_stream(&side, fn)) != MOE_OK) return st;
+    CHECK_HIP(hipEventRecord(side.fork, s));
+    CHECK_HIP(hipStreamWaitEvent(side.stream, side.fork, 0));
+    CHECK_HIP(shared_expert(cfg, N, hidden, w->sh_w1, w->sh_w3, w->sh_w2, at<void>(ws, p.sh_h),
+                            static_cast<float*>(sh_out), side.stream));
+    CHECK_HIP(hipEventRecord(side.join, side.stream));
+  }
+
+  // router on the full-width input
   st = run_route(cfg, N, hidden, w->w_router, w->bias, idx, wts, ws, p, s, fn);
   if (st != MOE_OK) return st;
   CHECK_HIP(mark(MOE_STAGE_ROUTED, s));
@@ -687,16 +810,9 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
   CHECK_HIP(moe::launch_dispatch_scatter(idx, N, (int)k, E, bits, base, perm, inv, s));
   CHECK_HIP(mark(MOE_STAGE_DISPATCHED, s));
 
-  // shared expert on the full-width input
-  void* sh_out = nullptr;
-  if (cfg->d_ff_shared > 0) {
-    void* sh_h = at<void>(ws, p.sh_h);
-    sh_out = at<void>(ws, p.sh_out);
-    CHECK_HIP(dense_gemm(cfg, hidden, N, d, w->sh_w1, w->sh_w3, cfg->d_ff_shared, sh_h,
-                         moe::EPI_GATE_UP, nullptr, s));
-    // the shared output stays in fp32 until the single final rounding
-    CHECK_HIP(dense_gemm(cfg, sh_h, N, cfg->d_ff_shared, w->sh_w2, nullptr, d, sh_out,
-                         is_bf16(cfg) ? moe::EPI_STORE_F32 : moe::EPI_STORE, nullptr, s));
+  if (cfg->d_ff_shared > 0 && !on_side) {
+    CHECK_HIP(shared_expert(cfg, N, hidden, w->sh_w1, w->sh_w3, w->sh_w2, at<void>(ws, p.sh_h),
+                            static_cast<float*>(sh_out), s));
   }
 
   CHECK_HIP(mark(MOE_STAGE_SHARED, s));
@@ -707,19 +823,23 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
   CHECK_HIP(grouped_gemm(cfg, p, N, x_in, moe::A_GATHER, perm, N, d_in, offsets, w->w1, w->w3,
                          cfg->d_ff, h, moe::EPI_GATE_UP, ws, s));
   CHECK_HIP(mark(MOE_STAGE_GATE_UP, s));
+  // down: each row written to its token's slot, so the combine reads a
+  // token's k rows contiguously
   CHECK_HIP(grouped_gemm(cfg, p, N, h, moe::A_DIRECT, nullptr, S, cfg->d_ff, offsets, w->w2,
-                         nullptr, d_in, out, moe::EPI_STORE, ws, s));
+                         nullptr, d_in, out, moe::EPI_STORE, ws, s, perm));
   CHECK_HIP(mark(MOE_STAGE_DOWN, s));
 
   if (L > 0) {
     void* y_lat = at<void>(ws, p.y_lat);
-    CHECK_HIP(moe::launch_combine_rmsnorm(out, inv, wts, w->gamma, cfg->norm_eps,
+    CHECK_HIP(moe::launch_combine_rmsnorm(out, nullptr, wts, w->gamma, cfg->norm_eps,
                                           cfg->latent_norm ? 1 : 0, y_lat, N, (int)k, L, S,
                                           is_bf16(cfg) ? 1 : 0, s));
+    if (on_side) CHECK_HIP(hipStreamWaitEvent(s, side.join, 0));
     CHECK_HIP(dense_gemm(cfg, y_lat, N, L, w->w_up, nullptr, d, y,
                          sh_out ? moe::EPI_STORE_RES : moe::EPI_STORE, sh_out, s));
   } else {
-    CHECK_HIP(moe::launch_combine(out, inv, wts, sh_out, 1, y, N, (int)k, d, S,
+    if (on_side) CHECK_HIP(hipStreamWaitEvent(s, side.join, 0));
+    CHECK_HIP(moe::launch_combine(out, nullptr, wts, sh_out, 1, y, N, (int)k, d, S,
                                   is_bf16(cfg) ? 1 : 0, s));
   }
   CHECK_HIP(mark(MOE_STAGE_END, s));

@@ -3,7 +3,9 @@
 // routing weights, the sum over the k slots, and for the latent block the
 // routed-expert norm that precedes the up projection).
 //
-// One work-group per token row.  The k expert rows are read through inv_perm,
+// One work-group per token row.  The k expert rows are read through inv_perm
+// (expert-sorted rows), or, when the down product has already written them in
+// slot order, as the token's k contiguous rows n k .. n k + k - 1; they are
 // multiplied by their weights and summed in fp32 in slot order j = 0..k-1 (a
 // fixed order: results do not depend on scheduling), a residual row (the
 // shared expert's output, kept in fp32 by the block) is added, and the sum is
@@ -83,9 +85,10 @@ __global__ __launch_bounds__(kThreads) void moe_combine(const void* __restrict__
   __shared__ float w[16];
   const int64_t n = blockIdx.x;
   if (threadIdx.x < k) {
-    int32_t p = inv_perm[n * k + threadIdx.x];
-    pos[threadIdx.x] = (p >= 0 && p < rows) ? p : -1;
-    w[threadIdx.x] = wts[n * k + threadIdx.x];
+    const int64_t slot = n * k + threadIdx.x;
+    const int64_t p = inv_perm ? inv_perm[slot] : slot;
+    pos[threadIdx.x] = (p >= 0 && p < rows) ? (int32_t)p : -1;
+    w[threadIdx.x] = wts[slot];
   }
   __syncthreads();
   for (int64_t c = (int64_t)threadIdx.x * kVec; c < width; c += kThreads * kVec) {
@@ -111,9 +114,10 @@ __global__ __launch_bounds__(kThreads) void moe_combine_rmsnorm(
   __shared__ float red[kThreads];
   const int64_t n = blockIdx.x;
   if (threadIdx.x < k) {
-    int32_t p = inv_perm[n * k + threadIdx.x];
-    pos[threadIdx.x] = (p >= 0 && p < rows) ? p : -1;
-    w[threadIdx.x] = wts[n * k + threadIdx.x];
+    const int64_t slot = n * k + threadIdx.x;
+    const int64_t p = inv_perm ? inv_perm[slot] : slot;
+    pos[threadIdx.x] = (p >= 0 && p < rows) ? (int32_t)p : -1;
+    w[threadIdx.x] = wts[slot];
   }
   __syncthreads();
   float acc[kMaxSteps][kVec];

@@ -74,6 +74,8 @@ struct GemmArgs {
   int64_t tile_cap;       // entries of tile_seg
   void* C;                // output
   int64_t ldc;
+  const int32_t* c_map;   // grouped EPI_STORE: row p of the product is written to row
+                          // c_map[p] of C (the slot order of the dispatch), or null
   int64_t c_rows;         // rows of C: tile rows at or past it are never touched
   const void* residual;   // EPI_STORE_RES: fp32 [rows, ld_res]
   int64_t ld_res;
@@ -87,6 +89,11 @@ struct GemmArgs {
 // grid capacity `mt_cap` m-tiles (grouped) is an upper bound of mt_off[S].
 hipError_t launch_gemm_bf16(const GemmArgs& a, int epi, int amode, int rb, int waves,
                             int64_t mt_cap, hipStream_t s);
+// bf16 MFMA GEMM for the dense products (one segment, A_DIRECT): 256 x 256
+// tiles on 8 waves.  gemm_dense_supported: whole 64-deep K blocks and aligned
+// rows; any EPI but the router's split-K fp32 partials.
+bool gemm_dense_supported(const GemmArgs& a, int epi);
+hipError_t launch_gemm_dense(const GemmArgs& a, int epi, hipStream_t s);
 // fp32 SIMT GEMM for fp32 blocks (64-row m-tiles).
 hipError_t launch_gemm_f32(const GemmArgs& a, int epi, int amode, int64_t mt_cap, hipStream_t s);
 int gemm_f32_rows_per_tile();
@@ -123,7 +130,8 @@ hipError_t launch_tiles_from_offsets(const int32_t* offsets, int64_t E, int rows
 
 // ---------------------------------------------------------------------------
 // Combine.
-// residual: [N, width] of the output type, or fp32 when res_f32 (or NULL)
+// inv_perm: row of slot n*k + j in out_sorted, or NULL when out holds the rows in
+// slot order; residual: [N, width] of the output type, or fp32 when res_f32 (or NULL)
 hipError_t launch_combine(const void* out_sorted, const int32_t* inv_perm, const float* w,
                           const void* residual, int res_f32, void* y, int64_t N, int k,
                           int64_t width, int64_t rows, int bf16, hipStream_t s);

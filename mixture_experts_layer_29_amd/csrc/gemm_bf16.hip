@@ -438,7 +438,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
             o[1] = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
             o[2] = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
             o[3] = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
-            *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(a.C) + orow * a.ldc + col) = o;
+            // slot order: the row goes to its token's slot (un-permuted here,
+            // so the combine reads each token's k rows contiguously)
+            const int64_t crow = (EPI == EPI_STORE && a.c_map) ? a.c_map[orow] : orow;
+            *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(a.C) + crow * a.ldc + col) = o;
           }
         }
       }

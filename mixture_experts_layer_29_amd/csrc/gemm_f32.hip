@@ -90,7 +90,8 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_f32(GemmArgs a, int64_t n_t
       float v = acc[0][i][j];
       if (EPI == EPI_GATE_UP) v = gemm::act_pair(a.act, acc[0][i][j], acc[1][i][j], a.beta, a.lbeta);
       if (EPI == EPI_STORE_RES) v += static_cast<const float*>(a.residual)[orow * a.ld_res + col];
-      static_cast<float*>(a.C)[orow * a.ldc + col] = v;
+      const int64_t crow = (EPI == EPI_STORE && a.c_map) ? a.c_map[orow] : orow;
+      static_cast<float*>(a.C)[crow * a.ldc + col] = v;
     }
   }
   }

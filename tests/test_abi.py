@@ -81,7 +81,7 @@ def test_good_config_and_workspace_sizes():
     assert binding.last_error() == ""
     assert m.moe_workspace_size(c, 0, m.CALL_BLOCK) >= 0
     assert m.moe_workspace_size(c, 64, m.CALL_COMBINE) == 0
-    sizes = [m.moe_workspace_size(c, 64, call) for call in range(6)]
+    sizes = [m.moe_workspace_size(c, 64, call) for call in range(6)]  # no shared / latent parts
     assert sizes[m.CALL_BLOCK] >= max(sizes[:5])
     with pytest.raises(m.MoeError):
         m.moe_workspace_size(c, -1, m.CALL_BLOCK)
@@ -148,6 +148,49 @@ def test_gathered_gate_up_argument_errors():
     assert st == binding.MOE_ERR_WORKSPACE
     assert lib.moe_expert_gate_up_gather(ctypes.byref(c), 0, None, None, None, None, None, None,
                                          None, 0, None) == binding.MOE_OK
+
+
+def test_down_scatter_argument_errors():
+    lib = binding.lib()
+    c = good(dtype=m.DTYPE_BF16)
+    st = lib.moe_expert_down_scatter(ctypes.byref(c), 8, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                     1 << 30, None)
+    assert st == binding.MOE_ERR_INVALID_ARG and "perm" in binding.last_error()
+    st = lib.moe_expert_down_scatter(ctypes.byref(c), 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+                                     None)
+    assert st == binding.MOE_ERR_WORKSPACE
+    assert lib.moe_expert_down_scatter(ctypes.byref(c), 0, None, None, None, None, None, None, 0,
+                                       None) == binding.MOE_OK
+    # the combine takes a NULL inv_perm (rows already in slot order) ...
+    assert lib.moe_combine(ctypes.byref(c), 0, None, None, None, None, None, None) == binding.MOE_OK
+    # ... but not a NULL weight array
+    st = lib.moe_combine(ctypes.byref(c), 8, FAKE, None, None, None, FAKE, None)
+    assert st == binding.MOE_ERR_INVALID_ARG and "topk_weight" in binding.last_error()
+
+
+def test_shared_and_latent_argument_errors():
+    lib = binding.lib()
+    c = good(dtype=m.DTYPE_BF16)  # no shared expert, no latent width
+    st = lib.moe_shared_expert(ctypes.byref(c), 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                               None)
+    assert st == binding.MOE_ERR_INVALID_ARG and "shared" in binding.last_error()
+    with pytest.raises(m.MoeError):
+        m.moe_workspace_size(c, 64, m.CALL_SHARED)
+    st = lib.moe_latent_project(ctypes.byref(c), 8, 0, FAKE, FAKE, None, FAKE, None)
+    assert st == binding.MOE_ERR_INVALID_ARG and "latent" in binding.last_error()
+    c2 = good(dtype=m.DTYPE_BF16, d_latent=64, d_ff_shared=32)
+    assert m.moe_workspace_size(c2, 64, m.CALL_SHARED) >= 64 * 32 * 2
+    assert m.moe_workspace_size(c2, 64, m.CALL_LATENT) == 0
+    st = lib.moe_shared_expert(ctypes.byref(c2), 8, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30,
+                               None)
+    assert st == binding.MOE_ERR_INVALID_ARG and "sh_w2" in binding.last_error()
+    st = lib.moe_shared_expert(ctypes.byref(c2), 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert st == binding.MOE_ERR_WORKSPACE
+    st = lib.moe_latent_project(ctypes.byref(c2), 8, 2, FAKE, FAKE, None, FAKE, None)
+    assert st == binding.MOE_ERR_INVALID_ARG
+    st = lib.moe_latent_project(ctypes.byref(c2), 8, 1, FAKE, FAKE, FAKE + 4, FAKE, None)
+    assert st == binding.MOE_ERR_INVALID_ARG and "residual" in binding.last_error()
+    assert lib.moe_latent_project(ctypes.byref(c2), 0, 1, None, None, None, None, None) == 0
 
 
 def test_binding_refuses_host_tensors():

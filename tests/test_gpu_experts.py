@@ -1,6 +1,8 @@
 """moe_expert_gate_up, moe_expert_down and moe_combine against the oracle's
 per-row expert halves and combine, on ragged widths, empty experts, a hot
-expert, and row counts that select each tile height of the grouped GEMM."""
+expert, and row counts that select each tile height of the grouped GEMM; the
+slot-order forms (moe_expert_down_scatter, moe_combine without inv_perm)
+against the sorted forms, bit for bit."""
 import numpy as np
 import pytest
 
@@ -90,6 +92,14 @@ def test_gate_up_and_down(name, N, E, k, d_in, d_ff, act, hot, empty, dtype):
     else:
         assert_close_f32(to_host(out), o_ref, "down")
 
+    # the slot-order form: the same products, row p stored at slot perm[p]
+    slots = torch.full((S, d_in), float("nan"), dtype=h.dtype, device="cuda")
+    m.moe_expert_down_scatter(cfg, N, to_device(hin, bf16), doffs, torch.from_numpy(perm).cuda(),
+                              dW["w2"], slots, m.workspace(cfg, N, m.CALL_DOWN))
+    torch.cuda.synchronize()
+    got_slots = to_host(slots)
+    assert np.array_equal(got_slots[perm], to_host(out)), "scattered rows differ from sorted rows"
+
 
 # Expert sizes chosen so that 256-row tiles hold every count of 32-row blocks,
 # 1 .. 8 (one expert spilling into a second m-tile): the activation ring's
@@ -166,3 +176,10 @@ def test_combine(N, k, width, residual, dtype):
         assert np.all(np.abs(got - y_ref) <= np.abs(y_ref) * 2.0 ** -8 + 1e-6)
     else:
         np.testing.assert_allclose(got, y_ref, rtol=1e-5, atol=1e-6)
+    # rows already in slot order (moe_expert_down_scatter): no inv_perm, the
+    # same sums in the same order, so the same bits
+    y2 = torch.empty_like(y)
+    m.moe_combine(cfg, N, to_device(np.ascontiguousarray(outs[inv]), bf16), None,
+                  torch.from_numpy(wts).cuda(), to_device(res, bf16) if residual else None, y2)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(y2), to_host(y))
