@@ -398,7 +398,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
                                             a.lbeta);
             o[e] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
           }
-          *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(a.C) + (t.row0 + tr) * a.ldc + col) = o;
+          bf16_t* const dst = static_cast<bf16_t*>(a.C) + (t.row0 + tr) * a.ldc + col;
+          if (a.c_write_through) {
+            // device-scope store: written through this XCD's L2, so a tile on
+            // any XCD may read it once the store has completed (the s_nop
+            // covers the wait state before a VALU may rewrite wide store data,
+            // which the compiler does not see inside inline asm)
+            asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" :: "v"(dst), "v"(o)
+                         : "memory");
+          } else {
+            *reinterpret_cast<u32x4*>(dst) = o;
+          }
         }
       }
     } else {
@@ -488,6 +498,83 @@ void moe_gemm_bf16(GemmArgs a, int64_t n_tiles_n) {
   }
 }
 
+// ---- both expert products in one persistent launch (decode) -------------
+// At decode every expert holds a few rows, one 32-row m-tile, and each tile is
+// one pass over a slice of its weights.  In two launches the down product
+// starts only after the last gate/up tile, and its first tiles fill the
+// pipeline again.  Here one work-group per CU takes tiles from its XCD's queue:
+// first the gate/up tiles of the XCD's run of experts (the same runs and
+// order as the grouped launches), then their down tiles.  A down tile needs
+// the h rows of its m-tile from every gate/up n-tile: a gate/up tile stores
+// its rows through to device scope, waits for the stores to complete and bumps
+// the m-tile's counter; a down tile waits until the counter holds all n-tiles.
+// (A release fence per tile instead writes back the XCD's whole L2 each time,
+// which measured 40% slower.)
+// Queue positions go to running work-groups only, in order, so the gate/up
+// tiles a down tile waits for are already running and the wait ends.  It is
+// bounded all the same: past kSpinLimit sleeps the tile runs and an error
+// flag is set.
+// sync: [0, 8) queue positions per XCD, [8] the error flag, [16, 16 + tile_cap)
+// the m-tile counters; all zero at launch.
+constexpr int kSpinLimit = 1 << 16;
+
+__device__ __forceinline__ int64_t mtile_of(const GemmArgs& a, const TileLoc& t) {
+  return a.mt_off[t.seg] + (t.row0 - a.seg_off[t.seg]) / 32;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void moe_expert_fused(GemmArgs gu, GemmArgs dn, int64_t n_gu, int64_t n_dn, int32_t* sync) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<1, 4>::kBytes];
+  int64_t* const s_q = reinterpret_cast<int64_t*>(smem);  // between tiles only
+  int32_t* const done = sync + 16;
+  const int x = blockIdx.x & 7;
+  const int32_t* xs = gu.mt_off + gu.n_seg + 1;
+  const int64_t mb0 = gu.mt_off[xs[x]], mb1 = gu.mt_off[xs[x + 1]];
+  const int64_t n_gu_tiles = (mb1 - mb0) * n_gu, total = n_gu_tiles + (mb1 - mb0) * n_dn;
+  for (;;) {
+    __syncthreads();  // the last tile is done with the LDS
+    if (threadIdx.x == 0)
+      *s_q = __hip_atomic_fetch_add(sync + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int64_t q = *static_cast<volatile int64_t*>(s_q);
+    __syncthreads();  // every wave holds q before the next tile fills the LDS
+    if (q >= total) break;
+    TileLoc t;
+    if (q < n_gu_tiles) {
+      if (!gemm::locate<32>(gu, mb0 * n_gu + q, n_gu, t)) continue;
+      gemm_tile<1, 1, 4, EPI_GATE_UP, A_GATHER, false>(gu, t, smem);
+      // the h rows were stored through to device scope (c_write_through):
+      // once every lane's stores have completed, the count may go up
+      lds::wait_vm<0>();
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(done + mtile_of(gu, t), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (!gemm::locate<32>(dn, mb0 * n_dn + (q - n_gu_tiles), n_dn, t)) continue;
+      if (threadIdx.x == 0) {
+        const int32_t* c = done + mtile_of(dn, t);
+        for (int spins = 0;
+             __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_gu; ++spins) {
+          if (spins >= kSpinLimit) {
+            __hip_atomic_store(sync + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      __syncthreads();
+      asm volatile("buffer_inv sc0" ::: "memory");  // no stale h lines in this CU's L1
+      gemm_tile<1, 1, 4, EPI_STORE, A_DIRECT, false>(dn, t, smem);
+    }
+  }
+}
+
+__global__ void moe_fill_zero(int32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
 template <int RB, int W, int EPI, int AMODE, bool KT>
 hipError_t launch_rb(const GemmArgs& a, int64_t mt_cap, hipStream_t s) {
   constexpr int CPW = (EPI == EPI_GATE_UP) ? 32 : 64;
@@ -539,6 +626,23 @@ hipError_t launch_any(const GemmArgs& a, int rb, int waves, int64_t mt_cap, hipS
 }
 
 }  // namespace
+
+bool expert_fused_supported(const GemmArgs& gu, const GemmArgs& dn) {
+  return gu.K % 64 == 0 && dn.K % 64 == 0 && gu.seg_off && dn.seg_off && gu.mt_off == dn.mt_off;
+}
+
+hipError_t launch_expert_fused(const GemmArgs& gu, const GemmArgs& dn, int32_t* sync,
+                               int64_t tile_cap, int n_wg, hipStream_t s) {
+  const int64_t n = 16 + tile_cap;
+  moe_fill_zero<<<dim3((unsigned)((n + 255) / 256 < 64 ? (n + 255) / 256 : 64)), dim3(256), 0, s>>>(
+      sync, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n_gu = (gu.n_cols + kPairs * 32 - 1) / (kPairs * 32);
+  const int64_t n_dn = (dn.n_cols + kPairs * 64 - 1) / (kPairs * 64);
+  moe_expert_fused<<<dim3((unsigned)n_wg), dim3(256), 0, s>>>(gu, dn, n_gu, n_dn, sync);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int epi, int amode, int rb, int waves,
                             int64_t mt_cap, hipStream_t s) {
