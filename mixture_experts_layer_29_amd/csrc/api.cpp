@@ -435,17 +435,18 @@ moe_status static_scratch(void** out, const char* fn) {
   return MOE_OK;
 }
 
-// The block runs its shared expert on a side stream of the device, beside
-// the routed path: the shared expert's products are bound by the matrix
-// cores, the routed expert GEMMs by HBM, so the two share the GPU better than
-// they run one after the other.  One side stream (default priority) and a
-// fork/join event pair per device, created on first use and kept until the
-// process ends.  A block call holds g_side_mutex from its fork to its join,
-// so concurrent calls do not interleave their records of the two events.
+// The block runs the products that need only its input -- the latent down
+// projection, then the shared expert -- on a side stream of the device, beside
+// the router and the dispatch, whose kernels are few and short: the dense
+// products fill the CUs they leave idle.  One side stream (default priority)
+// and its events per device (fork; latent input ready; shared output ready),
+// created on first use and kept until the process ends.  A block call holds
+// g_side_mutex from its fork to its last wait, so concurrent calls do not
+// interleave their records of the events.
 constexpr bool kSharedOnSide = true;
 struct Side {
   hipStream_t stream;
-  hipEvent_t fork, join;
+  hipEvent_t fork, latent, join;
 };
 std::mutex g_side_mutex;
 Side g_side[kMaxDevices] = {};
@@ -482,6 +483,7 @@ moe_status side_stream(Side* out, const char* fn) {
     Side n{};
     CHECK_HIP(hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking));
     CHECK_HIP(hipEventCreateWithFlags(&n.fork, hipEventDisableTiming));
+    CHECK_HIP(hipEventCreateWithFlags(&n.latent, hipEventDisableTiming));
     CHECK_HIP(hipEventCreateWithFlags(&n.join, hipEventDisableTiming));
     sd = n;
   }
@@ -800,22 +802,31 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
   int32_t* perm = at<int32_t>(ws, p.perm);
   int32_t* inv = at<int32_t>(ws, p.inv_perm);
 
-  // shared expert on the full-width input, forked to the side stream (or run
-  // in line below); joined before the output that adds it
+  // latent down projection and shared expert on the full-width input, forked
+  // to the side stream (or run in line below); the routed GEMMs wait for the
+  // latent input, the output that adds the shared expert for its output
   CHECK_HIP(mark(MOE_STAGE_BEGIN, s));
   void* sh_out = nullptr;
+  void* x_lat = L > 0 ? at<void>(ws, p.x_lat) : nullptr;
   std::unique_lock<std::mutex> side_lock;
   Side side{};
-  const bool on_side = kSharedOnSide && cfg->d_ff_shared > 0;
+  const bool on_side = kSharedOnSide && (L > 0 || cfg->d_ff_shared > 0);
   if (cfg->d_ff_shared > 0) sh_out = at<void>(ws, p.sh_out);
   if (on_side) {
     side_lock = std::unique_lock<std::mutex>(g_side_mutex);
     if ((st = side_stream(&side, fn)) != MOE_OK) return st;
     CHECK_HIP(hipEventRecord(side.fork, s));
     CHECK_HIP(hipStreamWaitEvent(side.stream, side.fork, 0));
-    CHECK_HIP(shared_expert(cfg, N, hidden, w->sh_w1, w->sh_w3, w->sh_w2, at<void>(ws, p.sh_h),
-                            static_cast<float*>(sh_out), side.stream));
-    CHECK_HIP(hipEventRecord(side.join, side.stream));
+    if (L > 0) {
+      CHECK_HIP(dense_gemm(cfg, hidden, N, d, w->w_down, nullptr, L, x_lat, moe::EPI_STORE,
+                           nullptr, side.stream));
+      CHECK_HIP(hipEventRecord(side.latent, side.stream));
+    }
+    if (cfg->d_ff_shared > 0) {
+      CHECK_HIP(shared_expert(cfg, N, hidden, w->sh_w1, w->sh_w3, w->sh_w2,
+                              at<void>(ws, p.sh_h), static_cast<float*>(sh_out), side.stream));
+      CHECK_HIP(hipEventRecord(side.join, side.stream));
+    }
   }
 
   // router on the full-width input
@@ -823,13 +834,10 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
   if (st != MOE_OK) return st;
   CHECK_HIP(mark(MOE_STAGE_ROUTED, s));
 
-  // latent down projection
-  const void* x_in = hidden;
-  if (L > 0) {
-    void* x_lat = at<void>(ws, p.x_lat);
+  // latent down projection (in line when not on the side stream)
+  const void* x_in = L > 0 ? x_lat : hidden;
+  if (L > 0 && !on_side)
     CHECK_HIP(dense_gemm(cfg, hidden, N, d, w->w_down, nullptr, L, x_lat, moe::EPI_STORE, nullptr, s));
-    x_in = x_lat;
-  }
   CHECK_HIP(mark(MOE_STAGE_LATENT, s));
 
   // dispatch
@@ -842,6 +850,7 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
   CHECK_HIP(moe::launch_dispatch_scatter(idx, N, (int)k, E, bits, base, perm, inv, s));
   CHECK_HIP(mark(MOE_STAGE_DISPATCHED, s));
 
+  if (L > 0 && on_side) CHECK_HIP(hipStreamWaitEvent(s, side.latent, 0));
   if (cfg->d_ff_shared > 0 && !on_side) {
     CHECK_HIP(shared_expert(cfg, N, hidden, w->sh_w1, w->sh_w3, w->sh_w2, at<void>(ws, p.sh_h),
                             static_cast<float*>(sh_out), s));
@@ -881,11 +890,11 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
     CHECK_HIP(moe::launch_combine_rmsnorm(out, nullptr, wts, w->gamma, cfg->norm_eps,
                                           cfg->latent_norm ? 1 : 0, y_lat, N, (int)k, L, S,
                                           is_bf16(cfg) ? 1 : 0, s));
-    if (on_side) CHECK_HIP(hipStreamWaitEvent(s, side.join, 0));
+    if (on_side && sh_out) CHECK_HIP(hipStreamWaitEvent(s, side.join, 0));
     CHECK_HIP(dense_gemm(cfg, y_lat, N, L, w->w_up, nullptr, d, y,
                          sh_out ? moe::EPI_STORE_RES : moe::EPI_STORE, sh_out, s));
   } else {
-    if (on_side) CHECK_HIP(hipStreamWaitEvent(s, side.join, 0));
+    if (on_side && sh_out) CHECK_HIP(hipStreamWaitEvent(s, side.join, 0));
     CHECK_HIP(moe::launch_combine(out, nullptr, wts, sh_out, 1, y, N, (int)k, d, S,
                                   is_bf16(cfg) ? 1 : 0, s));
   }
