@@ -250,11 +250,6 @@ def main():
     sec = ms_per_step / 1e3
     gu_ms = stage_ms["gate_up"]
     dn_ms = stage_ms["down"]
-    # decode-sized blocks run both expert products in one launch, timed as the
-    # gate/up stage (the down stage is empty): its bytes are both products'
-    fused = dn_ms < 0.01 * gu_ms
-    if fused:
-        gu_bytes, dn_bytes = gu_bytes + dn_bytes, 0
     gu_gbs = gu_bytes / (gu_ms / 1e3) / 1e9
     traffic = traffic_entry(w.name, "gate_up")
     out = {
@@ -284,9 +279,8 @@ def main():
         "tokens_per_expert": {"min": int(cnt.min()), "max": int(cnt.max()),
                               "mean": float(cnt.mean())},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "roofline": {"kernel": ("moe_expert_fused (routed gate/up and down in one launch)"
-                                if fused else "moe_gemm_bf16 (routed gate/up, gathered rows, "
-                                f"{w.act} epilogue)"),
+        "roofline": {"kernel": "moe_gemm_bf16 (routed gate/up, gathered rows, "
+                               f"{w.act} epilogue)",
                      "bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gu_gbs / HBM_PEAK_GBS,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
@@ -295,11 +289,10 @@ def main():
                          "gathered_rows": impl["gate_up_gathered_rows"],
                          "h_written": impl["gate_up_h_written"]},
                      "traffic_source": traffic["source"] if traffic else None},
+        "routed_down": {"achieved": dn_bytes / (dn_ms / 1e3) / 1e9, "unit": "GB/s",
+                        "frac": dn_bytes / (dn_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                        "algorithmic_bytes_per_launch": dn_bytes, "avg_launch_ms": dn_ms},
     }
-    if not fused:
-        out["routed_down"] = {"achieved": dn_bytes / (dn_ms / 1e3) / 1e9, "unit": "GB/s",
-                              "frac": dn_bytes / (dn_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                              "algorithmic_bytes_per_launch": dn_bytes, "avg_launch_ms": dn_ms}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

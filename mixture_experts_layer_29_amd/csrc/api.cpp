@@ -130,8 +130,7 @@ struct Plan {
   size_t bytes = 0;
   size_t w_split = 0, logits = 0, idx = 0, wts = 0, bits = 0, base = 0, counts = 0, offsets = 0;
   size_t mt_off = 0, tile_seg = 0, perm = 0, inv_perm = 0, x_lat = 0, h = 0, out = 0;
-  size_t sh_h = 0, sh_out = 0, y_lat = 0, sync = 0;
-  bool fused = false;      // decode: both expert products in one launch (bf16, 32-row tiles)
+  size_t sh_h = 0, sh_out = 0, y_lat = 0;
   int rb = 4;              // row blocks of 32 per grouped-GEMM tile (bf16)
   int waves_gate_up = 4;   // waves per grouped-GEMM work-group (bf16), gate/up
   int waves_down = 4;      //   and down products
@@ -256,8 +255,6 @@ Plan make_plan(const moe_config* c, int64_t N, int call) {
       p.sh_h = cv.take((size_t)N * c->d_ff_shared * es);
       p.sh_out = cv.take((size_t)N * c->d * 4);  // fp32: added before the final rounding
     }
-    p.fused = is_bf16(c) && p.rb == 1 && d_in % 64 == 0 && c->d_ff % 64 == 0;
-    if (p.fused) p.sync = cv.take((size_t)(16 + p.tile_cap) * 4);
   }
   p.bytes = cv.off;
   return p;
@@ -450,26 +447,6 @@ struct Side {
 };
 std::mutex g_side_mutex;
 Side g_side[kMaxDevices] = {};
-
-// Compute units of the current device (one persistent work-group each).
-std::mutex g_cu_mutex;
-int g_cus[kMaxDevices] = {};
-
-moe_status cu_count(int* out, const char* fn) {
-  int dev = -1;
-  CHECK_HIP(hipGetDevice(&dev));
-  if (dev < 0 || dev >= kMaxDevices)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d is beyond the %d supported", fn, dev,
-                kMaxDevices);
-  std::lock_guard<std::mutex> lock(g_cu_mutex);
-  if (!g_cus[dev]) {
-    int n = 0;
-    CHECK_HIP(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev));
-    g_cus[dev] = n > 0 ? n : 1;
-  }
-  *out = g_cus[dev];
-  return MOE_OK;
-}
 
 // The current device's side stream; the caller holds g_side_mutex.
 moe_status side_stream(Side* out, const char* fn) {
@@ -863,27 +840,12 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
   void* out = at<void>(ws, p.out);
   // down: each row written to its token's slot, so the combine reads a
   // token's k rows contiguously
-  moe::GemmArgs gu = grouped_args(cfg, p, N, x_in, perm, N, d_in, offsets, w->w1, w->w3,
-                                  cfg->d_ff, h, ws, nullptr);
-  gu.c_write_through = p.fused ? 1 : 0;
-  const moe::GemmArgs dn = grouped_args(cfg, p, N, h, nullptr, S, cfg->d_ff, offsets, w->w2,
-                                        nullptr, d_in, out, ws, perm);
-  if (p.fused && moe::expert_fused_supported(gu, dn)) {
-    // decode: one launch for both products (its time is reported as gate/up)
-    int cus = 0;
-    if ((st = cu_count(&cus, fn)) != MOE_OK) return st;
-    CHECK_HIP(moe::launch_expert_fused(gu, dn, at<int32_t>(ws, p.sync), p.tile_cap,
-                                       (cus + 7) / 8 * 8, s));
-    CHECK_HIP(mark(MOE_STAGE_GATE_UP, s));
-    CHECK_HIP(mark(MOE_STAGE_DOWN, s));
-  } else {
-    CHECK_HIP(grouped_gemm(cfg, p, N, x_in, moe::A_GATHER, perm, N, d_in, offsets, w->w1, w->w3,
-                           cfg->d_ff, h, moe::EPI_GATE_UP, ws, s));
-    CHECK_HIP(mark(MOE_STAGE_GATE_UP, s));
-    CHECK_HIP(grouped_gemm(cfg, p, N, h, moe::A_DIRECT, nullptr, S, cfg->d_ff, offsets, w->w2,
-                           nullptr, d_in, out, moe::EPI_STORE, ws, s, perm));
-    CHECK_HIP(mark(MOE_STAGE_DOWN, s));
-  }
+  CHECK_HIP(grouped_gemm(cfg, p, N, x_in, moe::A_GATHER, perm, N, d_in, offsets, w->w1, w->w3,
+                         cfg->d_ff, h, moe::EPI_GATE_UP, ws, s));
+  CHECK_HIP(mark(MOE_STAGE_GATE_UP, s));
+  CHECK_HIP(grouped_gemm(cfg, p, N, h, moe::A_DIRECT, nullptr, S, cfg->d_ff, offsets, w->w2,
+                         nullptr, d_in, out, moe::EPI_STORE, ws, s, perm));
+  CHECK_HIP(mark(MOE_STAGE_DOWN, s));
 
   if (L > 0) {
     void* y_lat = at<void>(ws, p.y_lat);

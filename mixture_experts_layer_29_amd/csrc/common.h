@@ -76,8 +76,6 @@ struct GemmArgs {
   int64_t ldc;
   const int32_t* c_map;   // grouped EPI_STORE: row p of the product is written to row
                           // c_map[p] of C (the slot order of the dispatch), or null
-  int32_t c_write_through;// EPI_GATE_UP: stores of C at device scope (read by other
-                          // tiles of the same launch)
   int64_t c_rows;         // rows of C: tile rows at or past it are never touched
   const void* residual;   // EPI_STORE_RES: fp32 [rows, ld_res]
   int64_t ld_res;
@@ -91,13 +89,6 @@ struct GemmArgs {
 // grid capacity `mt_cap` m-tiles (grouped) is an upper bound of mt_off[S].
 hipError_t launch_gemm_bf16(const GemmArgs& a, int epi, int amode, int rb, int waves,
                             int64_t mt_cap, hipStream_t s);
-// Decode: the gate/up (gathered rows, EPI_GATE_UP) and down (EPI_STORE) grouped
-// products of 32-row m-tiles in one persistent launch of n_wg work-groups (a
-// multiple of 8), the down tiles of an m-tile after its gate/up tiles.  sync:
-// 16 + tile_cap int32 of scratch, cleared by the launch.
-bool expert_fused_supported(const GemmArgs& gu, const GemmArgs& dn);
-hipError_t launch_expert_fused(const GemmArgs& gu, const GemmArgs& dn, int32_t* sync,
-                               int64_t tile_cap, int n_wg, hipStream_t s);
 // bf16 MFMA GEMM for the dense products (one segment, A_DIRECT): 256 x 256
 // tiles on 8 waves.  gemm_dense_supported: whole 64-deep K blocks and aligned
 // rows; any EPI but the router's split-K fp32 partials.

@@ -72,19 +72,20 @@ constexpr int kLdsOut = 72;                         // fp32 per LDS epilogue row
 // gfx950).  Eight waves pay off when the tiles are mostly full.
 //
 // LDS of an RB-block kernel: the largest plan of its tiles, or the epilogue.
-template <int RB, int W = 4>
+template <int RB, int W = 4, int LDS = kLdsMax>
 struct Smem {
-  static constexpr int ring_max(int nr) {
-    return nr == 0 ? 0 : (ring_bytes(nr) > ring_max(nr - 1) ? ring_bytes(nr) : ring_max(nr - 1));
-  }
-  static constexpr int ring_bytes(int nr) {
-    return nr == 1 ? Ring<1>::kBytes : nr == 2 ? Ring<2>::kBytes : nr == 3 ? Ring<3>::kBytes
-         : nr == 4 ? Ring<4>::kBytes : nr == 5 ? Ring<5>::kBytes : nr == 6 ? Ring<6>::kBytes
-         : nr == 7 ? Ring<7>::kBytes : Ring<8>::kBytes;
+  template <int NR>
+  static constexpr int ring_max() {
+    if constexpr (NR == 0) {
+      return 0;
+    } else {
+      constexpr int b = Ring<NR, LDS>::kBytes, r = ring_max<NR - 1>();
+      return b > r ? b : r;
+    }
   }
   static constexpr int kEpi = W * 32 * kLdsOut * 4;
-  static constexpr int kBytes = ring_max(RB) > kEpi ? ring_max(RB) : kEpi;
-  static_assert(kBytes <= kLdsMax, "LDS plan exceeds one CU");
+  static constexpr int kBytes = ring_max<RB>() > kEpi ? ring_max<RB>() : kEpi;
+  static_assert(kBytes <= LDS, "LDS plan exceeds the budget");
 };
 
 // NR: 32-row blocks holding rows.  The weight ring has SB = Smem<RB>::kSB
@@ -94,16 +95,16 @@ struct Smem {
 // first ceil(NR/2) and the last floor(NR/2)).  It also loads NRH of the
 // tile's 4 NR activation loads (8 rows each) and 4 * 4 / (W / 4) of its
 // column pair's weight loads per sub-block.
-template <int NR, int NRH, int W, int RB, int EPI, int AMODE, bool KT>
+template <int NR, int NRH, int W, int RB, int EPI, int AMODE, bool KT, int LDS>
 __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, uint8_t* smem,
                                           const int cw, const int h) {
-  constexpr int SB = Ring<NR>::kNB;        // weight stages
-  constexpr int NA = Ring<NR>::kNA;        // activation stages
+  constexpr int SB = Ring<NR, LDS>::kNB;   // weight stages
+  constexpr int NA = Ring<NR, LDS>::kNA;   // activation stages
   constexpr int kBL = W == 8 ? 2 : 4;      // weight loads per wave per sub-block
   constexpr int NRA = NRH > 0 ? NRH : 1;   // array extents
   constexpr int C0 = W == 8 ? (NR + 1) / 2 : NR;  // row blocks of the h = 0 wave
   constexpr int CPW = (EPI == EPI_GATE_UP) ? 32 : 64;  // output columns per wave
-  constexpr int ATILE = Ring<NR>::kATile;
+  constexpr int ATILE = Ring<NR, LDS>::kATile;
   uint8_t* const As = smem;                            // [NA][NR*32 rows][128 B]
   uint8_t* const Bs = smem + NA * ATILE;               // [SB][pair][32 rows][128 B]
 
@@ -231,9 +232,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
   const int cbase = (lane >> 5) * 4;
   // The activation fragments of a K block stay in registers for its second
   // sub-block while they fit next to the accumulators (up to 6 row blocks
-  // with W = 4, 3 with W = 8, which has half the registers); beyond that they
-  // are read again.
-  constexpr bool kKeepA = NRH <= (W == 4 ? 6 : 3);
+  // with W = 4, 3 with W = 8, which has half the registers, and 2 with W = 4
+  // at two work-groups per CU, which also has half); beyond that they are
+  // read again.
+  constexpr bool kKeepA = NRH <= (W == 4 ? (LDS == kLdsMax ? 6 : 2) : 3);
   bf16x8 afk[kKeepA ? 4 : 2][NRA];  // activation fragments (all steps, or two)
   auto compute0 = [&](auto col_tag, const uint8_t* at, const uint8_t* bt) {
     constexpr int COL = decltype(col_tag)::value;
@@ -398,17 +400,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
                                             a.lbeta);
             o[e] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
           }
-          bf16_t* const dst = static_cast<bf16_t*>(a.C) + (t.row0 + tr) * a.ldc + col;
-          if (a.c_write_through) {
-            // device-scope store: written through this XCD's L2, so a tile on
-            // any XCD may read it once the store has completed (the s_nop
-            // covers the wait state before a VALU may rewrite wide store data,
-            // which the compiler does not see inside inline asm)
-            asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" :: "v"(dst), "v"(o)
-                         : "memory");
-          } else {
-            *reinterpret_cast<u32x4*>(dst) = o;
-          }
+          *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(a.C) + (t.row0 + tr) * a.ldc + col) = o;
         }
       }
     } else {
@@ -461,24 +453,28 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const TileLoc& t, u
   __syncthreads();  // the LDS is free for the next tile
 }
 
-template <int NR, int RB, int W, int EPI, int AMODE, bool KT>
+template <int NR, int RB, int W, int EPI, int AMODE, bool KT, int LDS = kLdsMax>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileLoc& t, uint8_t* smem) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (W == 4) {
-    gemm_body<NR, NR, 4, RB, EPI, AMODE, KT>(a, t, smem, wave, 0);
+    gemm_body<NR, NR, 4, RB, EPI, AMODE, KT, LDS>(a, t, smem, wave, 0);
   } else {
-    if (wave < kPairs) gemm_body<NR, (NR + 1) / 2, 8, RB, EPI, AMODE, KT>(a, t, smem, wave, 0);
-    else gemm_body<NR, NR / 2, 8, RB, EPI, AMODE, KT>(a, t, smem, wave - kPairs, 1);
+    if (wave < kPairs) gemm_body<NR, (NR + 1) / 2, 8, RB, EPI, AMODE, KT, LDS>(a, t, smem, wave, 0);
+    else gemm_body<NR, NR / 2, 8, RB, EPI, AMODE, KT, LDS>(a, t, smem, wave - kPairs, 1);
   }
 }
 
 
-// The LDS plan fills a CU, so one work-group runs per CU: with 4 waves each
-// may use a SIMD's whole register file, with 8 waves half of it.
-template <int RB, int W, int EPI, int AMODE, bool KT>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4)))
+// With the whole LDS (LDS = kLdsMax) one work-group runs per CU: with 4 waves
+// each may use a SIMD's whole register file, with 8 waves half of it.  With
+// half of it (kLdsHalf, 4-wave tiles of up to 4 row blocks) two work-groups
+// share a CU, two waves per SIMD: while one fills its rings at a tile's start
+// or drains them into its epilogue, the other streams.
+template <int RB, int W, int EPI, int AMODE, bool KT, int LDS>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(
+    W / 4 * (LDS == kLdsMax ? 1 : 2), W / 4 * (LDS == kLdsMax ? 1 : 2))))
 void moe_gemm_bf16(GemmArgs a, int64_t n_tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<RB, W>::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<RB, W, LDS>::kBytes];
   int64_t L, end, step;
   gemm::tile_range<RB * 32>(a, blockIdx.x, gridDim.x, n_tiles_n, L, end, step);
   for (; L < end; L += step) {
@@ -486,96 +482,19 @@ void moe_gemm_bf16(GemmArgs a, int64_t n_tiles_n) {
   if (!gemm::locate<RB * 32>(a, L, n_tiles_n, t)) continue;
   const int nrb = (t.rows + 31) >> 5;
   switch (nrb) {
-    case 1: gemm_tile<1, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    case 2: if constexpr (RB >= 2) gemm_tile<2, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    case 3: if constexpr (RB >= 3) gemm_tile<3, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    case 4: if constexpr (RB >= 4) gemm_tile<4, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    case 5: if constexpr (RB >= 5) gemm_tile<5, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    case 6: if constexpr (RB >= 6) gemm_tile<6, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    case 7: if constexpr (RB >= 7) gemm_tile<7, RB, W, EPI, AMODE, KT>(a, t, smem); break;
-    default: if constexpr (RB >= 8) gemm_tile<8, RB, W, EPI, AMODE, KT>(a, t, smem); break;
+    case 1: gemm_tile<1, RB, W, EPI, AMODE, KT, LDS>(a, t, smem); break;
+    case 2: if constexpr (RB >= 2) gemm_tile<2, RB, W, EPI, AMODE, KT, LDS>(a, t, smem); break;
+    case 3: if constexpr (RB >= 3) gemm_tile<3, RB, W, EPI, AMODE, KT, LDS>(a, t, smem); break;
+    case 4: if constexpr (RB >= 4) gemm_tile<4, RB, W, EPI, AMODE, KT, LDS>(a, t, smem); break;
+    case 5: if constexpr (RB >= 5) gemm_tile<5, RB, W, EPI, AMODE, KT, LDS>(a, t, smem); break;
+    case 6: if constexpr (RB >= 6) gemm_tile<6, RB, W, EPI, AMODE, KT, LDS>(a, t, smem); break;
+    case 7: if constexpr (RB >= 7) gemm_tile<7, RB, W, EPI, AMODE, KT, LDS>(a, t, smem); break;
+    default: if constexpr (RB >= 8) gemm_tile<8, RB, W, EPI, AMODE, KT, LDS>(a, t, smem); break;
   }
   }
 }
 
-// ---- both expert products in one persistent launch (decode) -------------
-// At decode every expert holds a few rows, one 32-row m-tile, and each tile is
-// one pass over a slice of its weights.  In two launches the down product
-// starts only after the last gate/up tile, and its first tiles fill the
-// pipeline again.  Here one work-group per CU takes tiles from its XCD's queue:
-// first the gate/up tiles of the XCD's run of experts (the same runs and
-// order as the grouped launches), then their down tiles.  A down tile needs
-// the h rows of its m-tile from every gate/up n-tile: a gate/up tile stores
-// its rows through to device scope, waits for the stores to complete and bumps
-// the m-tile's counter; a down tile waits until the counter holds all n-tiles.
-// (A release fence per tile instead writes back the XCD's whole L2 each time,
-// which measured 40% slower.)
-// Queue positions go to running work-groups only, in order, so the gate/up
-// tiles a down tile waits for are already running and the wait ends.  It is
-// bounded all the same: past kSpinLimit sleeps the tile runs and an error
-// flag is set.
-// sync: [0, 8) queue positions per XCD, [8] the error flag, [16, 16 + tile_cap)
-// the m-tile counters; all zero at launch.
-constexpr int kSpinLimit = 1 << 16;
-
-__device__ __forceinline__ int64_t mtile_of(const GemmArgs& a, const TileLoc& t) {
-  return a.mt_off[t.seg] + (t.row0 - a.seg_off[t.seg]) / 32;
-}
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void moe_expert_fused(GemmArgs gu, GemmArgs dn, int64_t n_gu, int64_t n_dn, int32_t* sync) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<1, 4>::kBytes];
-  int64_t* const s_q = reinterpret_cast<int64_t*>(smem);  // between tiles only
-  int32_t* const done = sync + 16;
-  const int x = blockIdx.x & 7;
-  const int32_t* xs = gu.mt_off + gu.n_seg + 1;
-  const int64_t mb0 = gu.mt_off[xs[x]], mb1 = gu.mt_off[xs[x + 1]];
-  const int64_t n_gu_tiles = (mb1 - mb0) * n_gu, total = n_gu_tiles + (mb1 - mb0) * n_dn;
-  for (;;) {
-    __syncthreads();  // the last tile is done with the LDS
-    if (threadIdx.x == 0)
-      *s_q = __hip_atomic_fetch_add(sync + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int64_t q = *static_cast<volatile int64_t*>(s_q);
-    __syncthreads();  // every wave holds q before the next tile fills the LDS
-    if (q >= total) break;
-    TileLoc t;
-    if (q < n_gu_tiles) {
-      if (!gemm::locate<32>(gu, mb0 * n_gu + q, n_gu, t)) continue;
-      gemm_tile<1, 1, 4, EPI_GATE_UP, A_GATHER, false>(gu, t, smem);
-      // the h rows were stored through to device scope (c_write_through):
-      // once every lane's stores have completed, the count may go up
-      lds::wait_vm<0>();
-      __syncthreads();
-      if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(done + mtile_of(gu, t), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      if (!gemm::locate<32>(dn, mb0 * n_dn + (q - n_gu_tiles), n_dn, t)) continue;
-      if (threadIdx.x == 0) {
-        const int32_t* c = done + mtile_of(dn, t);
-        for (int spins = 0;
-             __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_gu; ++spins) {
-          if (spins >= kSpinLimit) {
-            __hip_atomic_store(sync + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-      }
-      __syncthreads();
-      asm volatile("buffer_inv sc0" ::: "memory");  // no stale h lines in this CU's L1
-      gemm_tile<1, 1, 4, EPI_STORE, A_DIRECT, false>(dn, t, smem);
-    }
-  }
-}
-
-__global__ void moe_fill_zero(int32_t* p, int64_t n) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0;
-}
-
-template <int RB, int W, int EPI, int AMODE, bool KT>
+template <int RB, int W, int EPI, int AMODE, bool KT, int LDS = kLdsMax>
 hipError_t launch_rb(const GemmArgs& a, int64_t mt_cap, hipStream_t s) {
   constexpr int CPW = (EPI == EPI_GATE_UP) ? 32 : 64;
   const int64_t n_tiles_n = (a.n_cols + kPairs * CPW - 1) / (kPairs * CPW);
@@ -585,7 +504,7 @@ hipError_t launch_rb(const GemmArgs& a, int64_t mt_cap, hipStream_t s) {
   const int64_t grid = gemm::round8(mt * n_tiles_n);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  moe_gemm_bf16<RB, W, EPI, AMODE, KT><<<dim3((unsigned)grid), dim3(64 * W), 0, s>>>(a, n_tiles_n);
+  moe_gemm_bf16<RB, W, EPI, AMODE, KT, LDS><<<dim3((unsigned)grid), dim3(64 * W), 0, s>>>(a, n_tiles_n);
   return hipGetLastError();
 }
 
@@ -602,14 +521,17 @@ hipError_t launch_any(const GemmArgs& a, int rb, int waves, int64_t mt_cap, hipS
     return hipErrorInvalidValue;
   }
   const bool w8 = waves == 8 && AMODE != A_REPEAT;
+  // 4-wave tiles of up to 4 row blocks share a CU two by two (half the LDS
+  // each); the router's product keeps the whole CU
+  constexpr int kHalf = AMODE == A_REPEAT ? kLdsMax : kLdsHalf;
   switch (rb) {
-    case 1: return launch_rb<1, 4, EPI, AMODE, false>(a, mt_cap, s);
-    case 2: return launch_rb<2, 4, EPI, AMODE, false>(a, mt_cap, s);
+    case 1: return launch_rb<1, 4, EPI, AMODE, false, kHalf>(a, mt_cap, s);
+    case 2: return launch_rb<2, 4, EPI, AMODE, false, kHalf>(a, mt_cap, s);
     case 4:
       if constexpr (AMODE != A_REPEAT) {
         if (w8) return launch_rb<4, 8, EPI, AMODE, false>(a, mt_cap, s);
       }
-      return launch_rb<4, 4, EPI, AMODE, false>(a, mt_cap, s);
+      return launch_rb<4, 4, EPI, AMODE, false, kHalf>(a, mt_cap, s);
     case 6:
       if constexpr (AMODE != A_REPEAT) return launch_rb<6, 4, EPI, AMODE, false>(a, mt_cap, s);
       return hipErrorInvalidValue;
@@ -626,23 +548,6 @@ hipError_t launch_any(const GemmArgs& a, int rb, int waves, int64_t mt_cap, hipS
 }
 
 }  // namespace
-
-bool expert_fused_supported(const GemmArgs& gu, const GemmArgs& dn) {
-  return gu.K % 64 == 0 && dn.K % 64 == 0 && gu.seg_off && dn.seg_off && gu.mt_off == dn.mt_off;
-}
-
-hipError_t launch_expert_fused(const GemmArgs& gu, const GemmArgs& dn, int32_t* sync,
-                               int64_t tile_cap, int n_wg, hipStream_t s) {
-  const int64_t n = 16 + tile_cap;
-  moe_fill_zero<<<dim3((unsigned)((n + 255) / 256 < 64 ? (n + 255) / 256 : 64)), dim3(256), 0, s>>>(
-      sync, n);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t n_gu = (gu.n_cols + kPairs * 32 - 1) / (kPairs * 32);
-  const int64_t n_dn = (dn.n_cols + kPairs * 64 - 1) / (kPairs * 64);
-  moe_expert_fused<<<dim3((unsigned)n_wg), dim3(256), 0, s>>>(gu, dn, n_gu, n_dn, sync);
-  return hipGetLastError();
-}
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int epi, int amode, int rb, int waves,
                             int64_t mt_cap, hipStream_t s) {

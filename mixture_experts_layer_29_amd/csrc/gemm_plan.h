@@ -13,22 +13,26 @@ constexpr int kBRows = 32;                          // weight rows of a column p
 constexpr int kBPair = kBRows * kRowBytes;          // 4 KB
 constexpr int kBStage = kPairs * kBPair;            // 16 KB
 constexpr int kLdsMax = 160 * 1024;                 // LDS of one CU
+constexpr int kLdsHalf = 80 * 1024;                 // half of it: two work-groups per CU
 
-// LDS plan of a tile with NR row blocks: NA activation stages of NR x 4 KB,
-// then as many 16 KB weight stages as fit (at most 9).  Loads complete in
-// issue order, so waiting for the activations of a K block also waits for
-// every weight load issued before them: the activations are issued NA - 1
-// K blocks (2 (NA - 1) sub-iterations) ahead, far enough that the wait for
-// them does not drain the weight loads in flight.  Short tiles afford four
-// activation stages, tall ones three.
-template <int NR>
+// LDS plan of a tile with NR row blocks in an LDS budget of LDS bytes: NA
+// activation stages of NR x 4 KB, then as many 16 KB weight stages as fit (at
+// most 9).  Loads complete in issue order, so waiting for the activations of
+// a K block also waits for every weight load issued before them: the
+// activations are issued NA - 1 K blocks (2 (NA - 1) sub-iterations) ahead,
+// far enough that the wait for them does not drain the weight loads in
+// flight.  With the whole CU, short tiles afford four activation stages, tall
+// ones three.  With half of it (two work-groups per CU, each covering the
+// other's tile start and end) the rings are shallower: 4, 3 or 2 activation
+// stages for 1, 2 or more row blocks, and 3 or 4 weight stages.
+template <int NR, int LDS = kLdsMax>
 struct Ring {
   static constexpr int kATile = NR * 32 * kRowBytes;
-  static constexpr int kNA = NR <= 5 ? 4 : 3;
-  static constexpr int kFit = (kLdsMax - kNA * kATile) / kBStage;
+  static constexpr int kNA = LDS == kLdsMax ? (NR <= 5 ? 4 : 3) : (NR <= 1 ? 4 : NR == 2 ? 3 : 2);
+  static constexpr int kFit = (LDS - kNA * kATile) / kBStage;
   static constexpr int kNB = kFit > 9 ? 9 : kFit;
   static constexpr int kBytes = kNA * kATile + kNB * kBStage;
-  static_assert(kNB >= 4 && kBytes <= kLdsMax, "LDS plan");
+  static_assert(kNB >= 3 && kBytes <= LDS, "LDS plan");
 };
 // vmcnt for the wait of sub-iteration u (even or odd, away from the start).
 // vmcnt counts a wave's loads in issue order, so the wait lets through the

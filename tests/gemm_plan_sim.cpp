@@ -166,9 +166,9 @@ int check_tight(int W, int NR, int NA, int NB, int NRH, int KBL, long nkb, int c
   return bad;
 }
 
-template <int NR>
+template <int NR, int LDS = kLdsMax>
 int check_nr(long nkb) {
-  constexpr int NA = Ring<NR>::kNA, NB = Ring<NR>::kNB;
+  constexpr int NA = Ring<NR, LDS>::kNA, NB = Ring<NR, LDS>::kNB;
   int bad = 0;
   // 4 waves: a wave owns all NR row blocks, 4 weight loads per sub-block
   bad += check_tight(4, NR, NA, NB, NR, 4, nkb, wait_count<4, NA, NB, NR, 4>(true),
@@ -189,7 +189,10 @@ int main() {
   for (long nkb : {1L, 2L, 3L, 4L, 5L, 7L, 16L, 32L, 112L}) {
     bad += check_nr<1>(nkb) + check_nr<2>(nkb) + check_nr<3>(nkb) + check_nr<4>(nkb) +
            check_nr<5>(nkb) + check_nr<6>(nkb) + check_nr<7>(nkb) + check_nr<8>(nkb);
-    cases += 8 * 3;
+    // the half-LDS plans of tiles that share a CU two by two (up to 4 row blocks)
+    bad += check_nr<1, kLdsHalf>(nkb) + check_nr<2, kLdsHalf>(nkb) +
+           check_nr<3, kLdsHalf>(nkb) + check_nr<4, kLdsHalf>(nkb);
+    cases += 12 * 3;
   }
   if (bad) {
     std::printf("%d failures\n", bad);

@@ -2,7 +2,8 @@
 
 gemm_plan_sim.cpp replays one wave's loads, vmcnt waits, barriers and LDS reads
 in the kernel's program order, for every tile height (1..8 row blocks), both
-wave layouts and K lengths from 1 to 112 blocks, and checks that every wait
+wave layouts, the whole-CU and the half-CU LDS plans (two work-groups per CU,
+up to 4 row blocks) and K lengths from 1 to 112 blocks, and checks that every wait
 lets through only loads younger than the ones its sub-iteration reads, that
 no stage is refilled before its last read (or, for stages several waves
 read, before a barrier after it), and that the counts are tight.  A plan

@@ -1,10 +1,9 @@
-"""The single-launch expert path of decode-sized blocks (every expert in one
-32-row m-tile or a few): moe_block_forward, which runs gate/up and down in one
-persistent launch there, against the same steps called one by one through the
-C ABI (route, permute, gathered gate/up, slot-order down, combine) -- the same
-tiles in the same K order, so the same bits -- and against the oracle.  The
-hot-expert cases give one expert two or three m-tiles, whose down tiles each
-wait for their own m-tile's gate/up tiles."""
+"""Decode-sized blocks (every expert in one 32-row m-tile or a few, the tiles
+two to a CU): moe_block_forward against the same steps called one by one
+through the C ABI (route, permute, gathered gate/up, slot-order down, combine)
+-- the same kernels on the same tiles, so the same bits -- and against the
+oracle.  The hot-expert cases give one expert two or three m-tiles; three
+calls in a row on one workspace give the same bits."""
 import numpy as np
 import pytest
 
@@ -57,9 +56,9 @@ def separate_calls(w, dev, cfg):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-def test_fused_decode(name):
+def test_decode_block(name):
     w, hot = CASES[name]
-    print(f"fused decode parity: {name} N={w.N} d={w.d} E={w.E} k={w.k} d_ff={w.d_ff}",
+    print(f"decode block parity: {name} N={w.N} d={w.d} E={w.E} k={w.k} d_ff={w.d_ff}",
           flush=True)
     m = moe()
     cfg = cfg_of(w)
@@ -77,7 +76,7 @@ def test_fused_decode(name):
         assert cnt.cpu().numpy()[hot] == w.N  # w.N / 32 m-tiles for one expert
     y2, idx2, wt2, cnt2 = separate_calls(w, dev, cfg)
     assert torch.equal(idx, idx2) and torch.equal(wt, wt2) and torch.equal(cnt, cnt2)
-    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "single launch != separate"
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "block != steps one by one"
     x = to_host(dev["hidden"])
     r_idx, r_w, _, _ = resolve_routing(x, to_host(dev["w_router"]), to_host(dev["bias"]), w,
                                        idx.cpu().numpy(), wt.cpu().numpy())
@@ -87,8 +86,8 @@ def test_fused_decode(name):
 
 
 def test_repeated_calls_reuse_the_workspace():
-    """The queue and m-tile counters live in the workspace and are cleared by
-    every call: three calls in a row on one workspace give the same bits."""
+    """Three calls in a row on one workspace give the same bits (the tile
+    tables and intermediates are rewritten by every call)."""
     w, hot = CASES["hot_two_mtiles"]
     m = moe()
     cfg = cfg_of(w)
