@@ -301,6 +301,12 @@ moe_status moe_latent_project(const moe_config* cfg, int64_t N, int32_t up, cons
  * rounding of y.  Intermediate roundings to dtype: the latent input x_in, each
  * expert's h and output rows, the shared expert's h, and the normalised
  * latent row.
+ * The latent down projection and the shared expert need only `hidden`: they
+ * run on a side stream of the current device (default priority, created on
+ * the first block call and kept until the process ends), forked from `stream`
+ * at the start of the call and joined back into it before the first step that
+ * uses their results, so the call's work is still complete when `stream`
+ * passes it.  Block calls of one process serialise on that side stream.
  * hidden [N, d] dtype.  Out: y [N, d] dtype.  Optional outputs (NULL skips):
  * topk_idx_out [N, k] int32, topk_weight_out [N, k] fp32,
  * tokens_per_expert_out [E] int32.
@@ -319,9 +325,11 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
 typedef enum {
   MOE_STAGE_BEGIN = 0,      /* before the router */
   MOE_STAGE_ROUTED = 1,     /* after the router (weight split, logits, selection) */
-  MOE_STAGE_LATENT = 2,     /* after the latent down projection */
+  MOE_STAGE_LATENT = 2,     /* after the latent down projection (empty on `stream`
+                               when it runs on the side stream) */
   MOE_STAGE_DISPATCHED = 3, /* after mask, scan and scatter */
-  MOE_STAGE_SHARED = 4,     /* after the shared expert */
+  MOE_STAGE_SHARED = 4,     /* after the wait for the latent input (the shared
+                               expert itself runs on the side stream) */
   MOE_STAGE_GATE_UP = 5,    /* after the routed gate/up grouped GEMM */
   MOE_STAGE_DOWN = 6,       /* after the routed down grouped GEMM */
   MOE_STAGE_END = 7,        /* after combine (and norm + up projection) */

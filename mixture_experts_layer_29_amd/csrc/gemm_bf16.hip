@@ -44,9 +44,14 @@
 //  - tiles are numbered segment-major, then n-tile, then m-tile; the experts
 //    are split into 8 runs of about equal cost, one per XCD, so the n-tiles
 //    of an expert share its activation rows in one L2;
+//  - a tile's fixed work (table lookups, ring ramp, epilogue) is up to an
+//    eighth of it: 4-wave tiles of up to 4 row blocks plan their rings in
+//    half the LDS and run two work-groups per CU, so that one streams while
+//    the other starts or ends a tile; taller tiles keep the whole CU;
 //  - the epilogue stages the fp32 accumulators through LDS, applies
 //    SiLU/SiTU-and-mul or the residual add in fp32, rounds once and writes
-//    16-byte row-contiguous chunks.
+//    16-byte row-contiguous chunks (for the down product of the block, to the
+//    rows' token slots).
 // Inside a 64-wide K block the lanes visit K in an order of our choosing, the
 // same for both operands (lane half h takes elements 32h .. 32h+31, eight per
 // MFMA step).
