@@ -440,7 +440,6 @@ moe_status static_scratch(void** out, const char* fn) {
 // created on first use and kept until the process ends.  A block call holds
 // g_side_mutex from its fork to its last wait, so concurrent calls do not
 // interleave their records of the events.
-constexpr bool kSharedOnSide = true;
 struct Side {
   hipStream_t stream;
   hipEvent_t fork, latent, join;
@@ -780,14 +779,14 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
   int32_t* inv = at<int32_t>(ws, p.inv_perm);
 
   // latent down projection and shared expert on the full-width input, forked
-  // to the side stream (or run in line below); the routed GEMMs wait for the
-  // latent input, the output that adds the shared expert for its output
+  // to the side stream; the routed GEMMs wait for the latent input, the output
+  // that adds the shared expert for its output
   CHECK_HIP(mark(MOE_STAGE_BEGIN, s));
   void* sh_out = nullptr;
   void* x_lat = L > 0 ? at<void>(ws, p.x_lat) : nullptr;
   std::unique_lock<std::mutex> side_lock;
   Side side{};
-  const bool on_side = kSharedOnSide && (L > 0 || cfg->d_ff_shared > 0);
+  const bool on_side = L > 0 || cfg->d_ff_shared > 0;
   if (cfg->d_ff_shared > 0) sh_out = at<void>(ws, p.sh_out);
   if (on_side) {
     side_lock = std::unique_lock<std::mutex>(g_side_mutex);
@@ -811,10 +810,7 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
   if (st != MOE_OK) return st;
   CHECK_HIP(mark(MOE_STAGE_ROUTED, s));
 
-  // latent down projection (in line when not on the side stream)
   const void* x_in = L > 0 ? x_lat : hidden;
-  if (L > 0 && !on_side)
-    CHECK_HIP(dense_gemm(cfg, hidden, N, d, w->w_down, nullptr, L, x_lat, moe::EPI_STORE, nullptr, s));
   CHECK_HIP(mark(MOE_STAGE_LATENT, s));
 
   // dispatch
@@ -827,11 +823,8 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
   CHECK_HIP(moe::launch_dispatch_scatter(idx, N, (int)k, E, bits, base, perm, inv, s));
   CHECK_HIP(mark(MOE_STAGE_DISPATCHED, s));
 
-  if (L > 0 && on_side) CHECK_HIP(hipStreamWaitEvent(s, side.latent, 0));
-  if (cfg->d_ff_shared > 0 && !on_side) {
-    CHECK_HIP(shared_expert(cfg, N, hidden, w->sh_w1, w->sh_w3, w->sh_w2, at<void>(ws, p.sh_h),
-                            static_cast<float*>(sh_out), s));
-  }
+  // the routed GEMMs read the latent input
+  if (L > 0) CHECK_HIP(hipStreamWaitEvent(s, side.latent, 0));
 
   CHECK_HIP(mark(MOE_STAGE_SHARED, s));
 
@@ -852,11 +845,11 @@ moe_status moe_block_forward(const moe_config* cfg, int64_t N, const moe_weights
     CHECK_HIP(moe::launch_combine_rmsnorm(out, nullptr, wts, w->gamma, cfg->norm_eps,
                                           cfg->latent_norm ? 1 : 0, y_lat, N, (int)k, L, S,
                                           is_bf16(cfg) ? 1 : 0, s));
-    if (on_side && sh_out) CHECK_HIP(hipStreamWaitEvent(s, side.join, 0));
+    if (sh_out) CHECK_HIP(hipStreamWaitEvent(s, side.join, 0));
     CHECK_HIP(dense_gemm(cfg, y_lat, N, L, w->w_up, nullptr, d, y,
                          sh_out ? moe::EPI_STORE_RES : moe::EPI_STORE, sh_out, s));
   } else {
-    if (on_side && sh_out) CHECK_HIP(hipStreamWaitEvent(s, side.join, 0));
+    if (sh_out) CHECK_HIP(hipStreamWaitEvent(s, side.join, 0));
     CHECK_HIP(moe::launch_combine(out, nullptr, wts, sh_out, 1, y, N, (int)k, d, S,
                                   is_bf16(cfg) ? 1 : 0, s));
   }
